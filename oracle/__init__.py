@@ -1,0 +1,171 @@
+"""CPU oracle for block-shared-exponent quantization -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (``block_scaled_bit_amd``)
+never touches it, and it never touches the product: the two share no code.
+
+The arithmetic lives in ``mxref.c`` (plain C, exact double precision, one
+block at a time); this module only marshals numpy arrays through ctypes.
+bf16 tensors are carried as ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+FP6_E2M3, FP6_E3M2, FP4_E2M1, FP8_E4M3, AXS6 = 0, 1, 2, 3, 4
+BF16, FP32 = 0, 1
+BLOCK = 32
+BYTES_PER_BLOCK = {FP6_E2M3: 24, FP6_E3M2: 24, FP4_E2M1: 16, FP8_E4M3: 32, AXS6: 24}
+CODE_BITS = {FP6_E2M3: 6, FP6_E3M2: 6, FP4_E2M1: 4, FP8_E4M3: 8, AXS6: 6}
+NAMES = {"mxfp6_e2m3": FP6_E2M3, "mxfp6_e3m2": FP6_E3M2, "mxfp4": FP4_E2M1,
+         "mxfp8": FP8_E4M3, "axs6": AXS6}
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.mxref_decode.argtypes = [I, I]
+    lib.mxref_decode.restype = ctypes.c_double
+    lib.mxref_encode.argtypes = [I, ctypes.c_double, I]
+    lib.mxref_encode.restype = I
+    lib.mxref_scale_byte.argtypes = [I, P, I]
+    lib.mxref_scale_byte.restype = I
+    lib.mxref_bytes_per_block.argtypes = [I]
+    lib.mxref_quantize.argtypes = [I, I, I, P, I64, I64, P, P, P]
+    lib.mxref_dequantize.argtypes = [I, I, P, P, P, I64, I64, I, P]
+    lib.mxref_fake_quantize.argtypes = [I, I, I, P, P, I64, I64]
+    lib.mxref_exp.argtypes = [ctypes.c_float]
+    lib.mxref_exp.restype = ctypes.c_float
+    lib.mxref_softmax_probs.argtypes = [P, I64, I64, P]
+    lib.mxref_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P]
+    for f in ("mxref_quantize", "mxref_dequantize", "mxref_fake_quantize",
+              "mxref_softmax_probs", "mxref_softmax_quantize"):
+        getattr(lib, f).restype = I
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(x: np.ndarray) -> int:
+    if x.dtype == np.uint16:
+        return BF16
+    if x.dtype == np.float32:
+        return FP32
+    raise TypeError(f"oracle input must be uint16 (bf16 bits) or float32, got {x.dtype}")
+
+
+def _rows_cols(x: np.ndarray):
+    if x.ndim == 0:
+        raise ValueError("need at least one dimension")
+    cols = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    return rows, cols
+
+
+def buffer_sizes(fmt: int, rows: int, cols: int):
+    nb = rows * (cols // BLOCK)
+    aux = (nb + 3) // 4 if fmt == AXS6 else 0
+    return nb * BYTES_PER_BLOCK[fmt], nb, aux
+
+
+def decode(fmt: int, code: int) -> float:
+    """Unscaled value of one element code (sign included)."""
+    return _lib.mxref_decode(fmt, int(code))
+
+
+def encode(fmt: int, v: float, byte: int) -> int:
+    """Element code of value v in a block with scale byte `byte`."""
+    return _lib.mxref_encode(fmt, float(v), int(byte))
+
+
+def scale_byte(fmt: int, values) -> int:
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    return _lib.mxref_scale_byte(fmt, _ptr(v), v.size)
+
+
+def quantize(fmt: int, x: np.ndarray):
+    """Returns (codes[rows, cols/32, bpb], scales[rows, cols/32], aux[ceil(nb/4)])."""
+    x = np.ascontiguousarray(x)
+    rows, cols = _rows_cols(x)
+    ncode, nb, naux = buffer_sizes(fmt, rows, cols)
+    codes = np.zeros(ncode, np.uint8)
+    scales = np.zeros(nb, np.uint8)
+    aux = np.zeros(max(naux, 1), np.uint8)
+    rc = _lib.mxref_quantize(fmt, BLOCK, _dtype_of(x), _ptr(x), rows, cols,
+                             _ptr(codes), _ptr(scales), _ptr(aux))
+    if rc:
+        raise ValueError("oracle quantize: bad arguments")
+    nbr = cols // BLOCK
+    return (codes.reshape(rows, nbr, BYTES_PER_BLOCK[fmt]), scales.reshape(rows, nbr),
+            aux[:naux])
+
+
+def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, aux, rows: int, cols: int,
+               out_dtype: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    auxa = np.ascontiguousarray(aux if aux is not None and len(aux) else np.zeros(1, np.uint8),
+                                dtype=np.uint8)
+    y = np.empty((rows, cols), np.uint16 if out_dtype == BF16 else np.float32)
+    rc = _lib.mxref_dequantize(fmt, BLOCK, _ptr(codes), _ptr(scales), _ptr(auxa), rows, cols,
+                               out_dtype, _ptr(y))
+    if rc:
+        raise ValueError("oracle dequantize: bad arguments")
+    return y
+
+
+def fake_quantize(fmt: int, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    rows, cols = _rows_cols(x)
+    y = np.empty_like(x)
+    rc = _lib.mxref_fake_quantize(fmt, BLOCK, _dtype_of(x), _ptr(x), _ptr(y), rows, cols)
+    if rc:
+        raise ValueError("oracle fake_quantize: bad arguments")
+    return y
+
+
+def exp_ref(d) -> np.ndarray:
+    d = np.asarray(d, dtype=np.float32)
+    out = np.empty_like(d)
+    flat_in, flat_out = d.reshape(-1), out.reshape(-1)
+    for i in range(flat_in.size):
+        flat_out[i] = _lib.mxref_exp(float(flat_in[i]))
+    return out
+
+
+def softmax_probs(s: np.ndarray) -> np.ndarray:
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    rows, cols = _rows_cols(s)
+    p = np.empty_like(s)
+    _lib.mxref_softmax_probs(_ptr(s), rows, cols, _ptr(p))
+    return p
+
+
+def softmax_quantize(fmt: int, s: np.ndarray):
+    """Row max, exp_ref(s - rowmax), block quantize: (codes, scales)."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    rows, cols = _rows_cols(s)
+    ncode, nb, _ = buffer_sizes(fmt, rows, cols)
+    codes = np.zeros(ncode, np.uint8)
+    scales = np.zeros(nb, np.uint8)
+    rc = _lib.mxref_softmax_quantize(fmt, BLOCK, _ptr(s), rows, cols, _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError("oracle softmax_quantize: bad arguments")
+    nbr = cols // BLOCK
+    return codes.reshape(rows, nbr, BYTES_PER_BLOCK[fmt]), scales.reshape(rows, nbr)

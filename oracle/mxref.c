@@ -1,0 +1,433 @@
+/*
+ * mxref.c -- plain, slow, obviously-correct CPU oracle for block-shared-
+ * exponent quantization (MXFP6 E2M3/E3M2, MXFP4 E2M1, MXFP8 E4M3, AXS-6).
+ *
+ * TEST INFRASTRUCTURE ONLY (see mxref.h).  Built with gcc -O2
+ * -ffp-contract=off, no fast-math.  Every rule below cites the page it
+ * follows; where the pages leave a step open the reading taken is named.
+ *
+ * Sources (titles of the pages):
+ *   [AXS6]  "AXS-6: Adaptive eXponent Sharing" (pitchhut project page)
+ *   [EXMY]  "eXmY: A Data Type and Technique for Arbitrary Bit Precision
+ *            Quantization" (abstract)
+ *   [EFQ]   "EFQ-Softmax: exp-free E2M1 probabilities" (explainer)
+ *   [MXFP6] "Online MXFP6" (Sonar feature page)
+ *
+ * Parity pins: format tables, scale rule, RNE/saturation, packing and
+ * dequantization are pinned by the CPU tests (library dtypes, brute-force
+ * nearest-code search, closed-form invariants).  The NaN/inf block rule,
+ * the bit order inside a packed block and the AXS-6 element/config
+ * semantics are readings of silent passages: parity unpinned by the pages,
+ * pinned only by the written rules here and their unit tests.
+ */
+#include "mxref.h"
+
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Element formats.                                                    */
+/* [MXFP6] "Start a model" / "Select the FP6 encoding": OCP MXFP6 with  */
+/* E2M3 (more mantissa) or E3M2 (more range), an E8M0 scale per 32.     */
+/* [EFQ] "Jargon": E2M1 = 1 sign, 2 exponent, 1 mantissa bit.           */
+/* [AXS6] "Overview": FP8 E4M3 = [sign:1][exponent:4][mantissa:3].      */
+/* Biases and ranges follow the OCP MX definitions the [MXFP6] page     */
+/* invokes by name (a reading: the pages print no bias).                */
+/* [AXS6] "Overview": [sign:1][mantissa:5] per value; read as a uniform */
+/* sign-magnitude grid m/16, m = 0..31, under the shared exponent.     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int bits;          /* code width including the sign bit */
+  int ebits, mbits;  /* exponent and mantissa field widths */
+  int bias;
+  int emin;          /* unbiased exponent of the smallest normal */
+  int emax;          /* floor(log2(largest finite value)) */
+  double maxnorm;    /* largest finite magnitude */
+  int nan_mag;       /* magnitude code meaning NaN, -1 if none */
+  int fixed_point;   /* 1: magnitude m means m/16 (AXS-6) */
+  int bpb;           /* packed bytes per 32-value block */
+} fmt_t;
+
+static const fmt_t FORMATS[5] = {
+    /* E2M3 */ {6, 2, 3, 1, 0, 2, 7.5, -1, 0, 24},
+    /* E3M2 */ {6, 3, 2, 3, -2, 4, 28.0, -1, 0, 24},
+    /* E2M1 */ {4, 2, 1, 1, 0, 2, 6.0, -1, 0, 16},
+    /* E4M3 */ {8, 4, 3, 7, -6, 8, 448.0, 0x7F, 0, 32},
+    /* AXS6 */ {6, 0, 5, 0, 0, 0, 31.0 / 16.0, -1, 1, 24},
+};
+
+#define BLOCK 32
+
+static const fmt_t *get_fmt(int fmt) {
+  return (fmt >= 0 && fmt <= 4) ? &FORMATS[fmt] : 0;
+}
+
+int mxref_bytes_per_block(int fmt) {
+  const fmt_t *f = get_fmt(fmt);
+  return f ? f->bpb : -1;
+}
+
+/* floor(log2(a)) for a finite a > 0, exactly */
+static int ilog2(double a) {
+  int e;
+  frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  return e - 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Decoding one code (sign included) to its unscaled value.            */
+/* ------------------------------------------------------------------ */
+double mxref_decode(int fmt, int code) {
+  const fmt_t *f = get_fmt(fmt);
+  int sign = (code >> (f->bits - 1)) & 1;
+  int mag = code & ((1 << (f->bits - 1)) - 1);
+  double v;
+  if (f->nan_mag >= 0 && mag == f->nan_mag) return NAN;
+  if (f->fixed_point) {
+    v = mag / 16.0;
+  } else {
+    int e = mag >> f->mbits;
+    int m = mag & ((1 << f->mbits) - 1);
+    if (e == 0) /* subnormal: m * 2^(emin - mbits) */
+      v = ldexp((double)m, f->emin - f->mbits);
+    else        /* normal: (1 + m/2^mbits) * 2^(e - bias) */
+      v = ldexp(1.0 + ldexp((double)m, -f->mbits), e - f->bias);
+  }
+  return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q1 + Q2: the shared scale of one block.                             */
+/* [EFQ] article: the block scale is exponent-only and is chosen from  */
+/* the block's local maximum; [EFQ] "Jargon": from that block alone.   */
+/* [MXFP6] "Start a model": an E8M0 scale per block of 32 values.      */
+/* Reading (OCP conversion rule): byte = floor(log2 amax) - emax + 127,*/
+/* clamped to 0..254; amax == 0 gives byte 0; any NaN or inf in the    */
+/* block gives 0xFF, E8M0's NaN (the element formats hold neither).    */
+/* AXS-6 uses the same rule with emax = 0 ([AXS6] "Overview": one      */
+/* 8-bit shared exponent per 32 values).                                */
+/* ------------------------------------------------------------------ */
+int mxref_scale_byte(int fmt, const double *v, int n) {
+  const fmt_t *f = get_fmt(fmt);
+  double amax = 0.0;
+  int i, b;
+  for (i = 0; i < n; i++) /* Q1: classify */
+    if (isnan(v[i]) || isinf(v[i])) return 0xFF;
+  for (i = 0; i < n; i++) /* Q2: absolute maximum */
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  if (amax == 0.0) return 0;
+  b = ilog2(amax) - f->emax + 127;
+  if (b < 0) b = 0;
+  if (b > 254) b = 254;
+  return b;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q3: one element.                                                    */
+/* a = |v| / 2^(byte-127) (exact); a is clamped to the largest finite  */
+/* magnitude (saturation, never NaN from a finite input); the code is  */
+/* the grid point nearest to a, ties to the code whose last bit is 0   */
+/* (round-to-nearest-even); the sign bit is copied, so -0 and negative */
+/* values that round to zero keep it.                                  */
+/* ------------------------------------------------------------------ */
+int mxref_encode(int fmt, double v, int byte) {
+  const fmt_t *f = get_fmt(fmt);
+  double X = ldexp(1.0, byte - 127);
+  double a = fabs(v) / X;
+  int sign = signbit(v) ? 1 : 0;
+  int mag;
+  if (a > f->maxnorm) a = f->maxnorm;
+  if (f->fixed_point) {
+    mag = (int)nearbyint(a * 16.0); /* step 1/16, RNE */
+    if (mag > 31) mag = 31;
+  } else if (a == 0.0) {
+    mag = 0;
+  } else {
+    int ea = ilog2(a);
+    int eu = ea > f->emin ? ea : f->emin;       /* binade of the step */
+    double u = ldexp(1.0, eu - f->mbits);       /* grid step at a */
+    double n = nearbyint(a / u);                /* RNE (default mode) */
+    double r = n * u;                           /* the chosen grid value */
+    if (r < ldexp(1.0, f->emin)) {              /* subnormal code */
+      mag = (int)(r / ldexp(1.0, f->emin - f->mbits));
+    } else {                                    /* normal code */
+      int er = ilog2(r);
+      int mant = (int)((r / ldexp(1.0, er) - 1.0) * (double)(1 << f->mbits));
+      mag = ((er + f->bias) << f->mbits) | mant;
+    }
+  }
+  return (sign << (f->bits - 1)) | mag;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q4: packing of one block's 32 codes.                                */
+/* [EXMY] abstract: non-power-of-two widths packed with no wasted bits */
+/* and byte addressability; [MXFP6] "Start a model": packed six-bit    */
+/* data.  Reading: the codes form a little-endian bit stream, code k   */
+/* at stream bits [k*w, k*w + w), stream bit s in bit s%8 of byte s/8. */
+/* For 6-bit codes every 4 codes fill 3 bytes; 4-bit codes put the     */
+/* even element in the low nibble; 8-bit codes are one per byte.       */
+/* ------------------------------------------------------------------ */
+static void pack_block(const fmt_t *f, const int *c, uint8_t *out) {
+  int k, j;
+  memset(out, 0, (size_t)f->bpb);
+  for (k = 0; k < BLOCK; k++)
+    for (j = 0; j < f->bits; j++) {
+      int s = k * f->bits + j;
+      if ((c[k] >> j) & 1) out[s / 8] |= (uint8_t)(1u << (s % 8));
+    }
+}
+
+static void unpack_block(const fmt_t *f, const uint8_t *in, int *c) {
+  int k, j;
+  for (k = 0; k < BLOCK; k++) {
+    c[k] = 0;
+    for (j = 0; j < f->bits; j++) {
+      int s = k * f->bits + j;
+      c[k] |= ((in[s / 8] >> (s % 8)) & 1) << j;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Host number formats: bf16 = top half of an fp32 bit pattern.         */
+/* ------------------------------------------------------------------ */
+static double load_value(int dtype, const void *x, int64_t i) {
+  uint32_t u;
+  float fv;
+  if (dtype == MXREF_BF16)
+    u = (uint32_t)((const uint16_t *)x)[i] << 16;
+  else
+    memcpy(&u, (const float *)x + i, 4);
+  memcpy(&fv, &u, 4);
+  return (double)fv;
+}
+
+/* Round a double to a binary format with p significand bits (hidden bit
+ * included) and normal exponents emin..emax, round-to-nearest-even,
+ * gradual underflow, overflow to infinity; return the IEEE bit pattern of
+ * the fp32 container (bf16 = top 16 bits).  NaN -> canonical quiet NaN. */
+static uint32_t round_to_bits(double y, int p) {
+  const int emin = -126, emax = 127;
+  uint32_t sign = signbit(y) ? 0x80000000u : 0u;
+  double ay = fabs(y), n, r;
+  int e, q;
+  uint32_t field, mant;
+  if (isnan(y)) return 0x7FC00000u;
+  if (ay == 0.0) return sign;
+  if (isinf(y)) return sign | 0x7F800000u;
+  e = ilog2(ay);
+  q = (e > emin ? e : emin) - (p - 1); /* exponent of one ulp */
+  n = nearbyint(ay / ldexp(1.0, q));
+  r = n * ldexp(1.0, q);
+  if (r >= ldexp(1.0, emax + 1)) return sign | 0x7F800000u;
+  if (r < ldexp(1.0, emin)) {
+    field = 0;
+    mant = (uint32_t)(r / ldexp(1.0, emin - (p - 1)));
+  } else {
+    int er = ilog2(r);
+    field = (uint32_t)(er + 127);
+    mant = (uint32_t)((r / ldexp(1.0, er) - 1.0) * ldexp(1.0, p - 1));
+  }
+  return sign | (field << 23) | (mant << (24 - p));
+}
+
+static void store_value(int dtype, void *y, int64_t i, double v) {
+  if (dtype == MXREF_BF16) {
+    uint32_t u = round_to_bits(v, 8);
+    ((uint16_t *)y)[i] = (uint16_t)(u >> 16);
+  } else {
+    uint32_t u = round_to_bits(v, 24);
+    memcpy((float *)y + i, &u, 4);
+  }
+}
+
+static int check_args(int fmt, int block, int64_t rows, int64_t cols) {
+  if (!get_fmt(fmt) || block != BLOCK) return -1;
+  if (rows < 0 || cols < 0 || cols % BLOCK) return -1;
+  return 0;
+}
+
+/* one block: Q1-Q3 on 32 doubles, codes into c[] */
+static int quantize_values(const fmt_t *f, int fmt, const double *v, int *c) {
+  int k, byte = mxref_scale_byte(fmt, v, BLOCK);
+  for (k = 0; k < BLOCK; k++)
+    c[k] = (byte == 0xFF) ? 0 : mxref_encode(fmt, v[k], byte);
+  (void)f;
+  return byte;
+}
+
+int mxref_quantize(int fmt, int block, int in_dtype, const void *x,
+                   int64_t rows, int64_t cols, uint8_t *codes,
+                   uint8_t *scales, uint8_t *aux) {
+  const fmt_t *f = get_fmt(fmt);
+  int64_t nb, b;
+  double v[BLOCK];
+  int c[BLOCK], k;
+  if (check_args(fmt, block, rows, cols)) return -1;
+  nb = rows * (cols / BLOCK);
+  for (b = 0; b < nb; b++) {
+    for (k = 0; k < BLOCK; k++) v[k] = load_value(in_dtype, x, b * BLOCK + k);
+    scales[b] = (uint8_t)quantize_values(f, fmt, v, c);
+    pack_block(f, c, codes + b * f->bpb);
+  }
+  /* [AXS6] "Overview": a 2-bit config field once per block.  Reading: the
+   * only configuration defined here is 0 (the uniform grid above). */
+  if (fmt == MXREF_AXS6)
+    for (b = 0; b < (nb + 3) / 4; b++) aux[b] = 0;
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* D: dequantize.  y = sign * decode(mag) * 2^(byte-127), exact, then  */
+/* rounded to the output type (RNE).  Byte 0xFF, an E4M3 NaN code, or  */
+/* an AXS-6 block whose config is not 0 decodes to canonical NaN.       */
+/* ------------------------------------------------------------------ */
+int mxref_dequantize(int fmt, int block, const uint8_t *codes,
+                     const uint8_t *scales, const uint8_t *aux, int64_t rows,
+                     int64_t cols, int out_dtype, void *y) {
+  const fmt_t *f = get_fmt(fmt);
+  int64_t nb, b;
+  int c[BLOCK], k;
+  if (check_args(fmt, block, rows, cols)) return -1;
+  nb = rows * (cols / BLOCK);
+  for (b = 0; b < nb; b++) {
+    int byte = scales[b];
+    int poisoned = (byte == 0xFF);
+    if (fmt == MXREF_AXS6 && ((aux[b / 4] >> (2 * (b % 4))) & 3) != 0)
+      poisoned = 1;
+    unpack_block(f, codes + b * f->bpb, c);
+    for (k = 0; k < BLOCK; k++) {
+      double val = poisoned ? NAN : mxref_decode(fmt, c[k]) * ldexp(1.0, byte - 127);
+      store_value(out_dtype, y, b * BLOCK + k, val);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* F: fake-quantize = dequantize(quantize(x)) in the input type, one   */
+/* block at a time with no packed intermediate ([AXS6] "Quick Start":  */
+/* fused_fake_quantize(x, block_size=32), no intermediate allocation). */
+/* ------------------------------------------------------------------ */
+int mxref_fake_quantize(int fmt, int block, int dtype, const void *x, void *y,
+                        int64_t rows, int64_t cols) {
+  const fmt_t *f = get_fmt(fmt);
+  int64_t nb, b;
+  double v[BLOCK];
+  int c[BLOCK], k, byte;
+  if (check_args(fmt, block, rows, cols)) return -1;
+  nb = rows * (cols / BLOCK);
+  for (b = 0; b < nb; b++) {
+    for (k = 0; k < BLOCK; k++) v[k] = load_value(dtype, x, b * BLOCK + k);
+    byte = quantize_values(f, fmt, v, c);
+    for (k = 0; k < BLOCK; k++) {
+      double val = (byte == 0xFF) ? NAN : mxref_decode(fmt, c[k]) * ldexp(1.0, byte - 127);
+      store_value(dtype, y, b * BLOCK + k, val);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* X: exp-then-quantize attention probabilities.                       */
+/* [EFQ] "Jargon" (shifted scores, exp-then-quantize) and the article: */
+/* subtract the row maximum, evaluate exp() in higher precision,       */
+/* materialize the probability block, then quantize it to block-scaled */
+/* E2M1.  Reading: "higher precision" is fp32 through the fixed op     */
+/* sequence mxref_exp below, so that a quantized code never depends on */
+/* which exp library ran.                                               */
+/* ------------------------------------------------------------------ */
+
+/* Cody-Waite range reduction (W. J. Cody and W. Waite, "Software Manual
+ * for the Elementary Functions", 1980) with a degree-7 Taylor polynomial:
+ *   n = rint(d * log2(e)),  r = d - n*ln2 (ln2 split in a 16-bit head and
+ *   a tail, each step one fused multiply-add),  p = sum_{k<=7} r^k / k!
+ *   by Horner's rule with fused multiply-adds,  exp(d) = p * 2^n.
+ * Constants: log2(e), ln2 and 1/k! each rounded to fp32; the head of ln2
+ * is ln2's fp32 significand cut to its top 16 bits, the tail is the fp32
+ * rounding of the remainder.  2^n is applied by exact multiplications by
+ * powers of two (two of them when 2^n alone is not a normal fp32), so the
+ * only rounding of the scaling is that of the final product. */
+float mxref_exp(float d) {
+  const float LOG2E = 0x1.715476p+0f;
+  const float LN2_HI = 0x1.62e400p-1f;
+  const float LN2_LO = 0x1.7f7d1cp-20f;
+  const float C2 = 0x1.000000p-1f, C3 = 0x1.555556p-3f, C4 = 0x1.555556p-5f,
+              C5 = 0x1.111112p-7f, C6 = 0x1.6c16c2p-10f, C7 = 0x1.a01a02p-13f;
+  float nf, r, p;
+  int n;
+  if (isnan(d)) return d;
+  if (d > 88.75f) return INFINITY;
+  if (d < -104.0f) return 0.0f;
+  nf = rintf(d * LOG2E);
+  r = fmaf(-nf, LN2_HI, d);
+  r = fmaf(-nf, LN2_LO, r);
+  p = C7;
+  p = fmaf(p, r, C6);
+  p = fmaf(p, r, C5);
+  p = fmaf(p, r, C4);
+  p = fmaf(p, r, C3);
+  p = fmaf(p, r, C2);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  n = (int)nf;
+  if (n < -100) { p = p * 0x1p-50f; n += 50; }
+  if (n > 100) { p = p * 0x1p+50f; n -= 50; }
+  return p * ldexpf(1.0f, n);
+}
+
+/* P = exp(s - rowmax) per row.  The row maximum is exact; a NaN anywhere
+ * in the row makes it NaN.  d = s - rowmax is one fp32 subtraction. */
+int mxref_softmax_probs(const float *s, int64_t rows, int64_t cols, float *p) {
+  int64_t r, i;
+  if (rows < 0 || cols < 0) return -1;
+  for (r = 0; r < rows; r++) {
+    const float *row = s + r * cols;
+    float m = -INFINITY;
+    int has_nan = 0;
+    for (i = 0; i < cols; i++) {
+      if (isnan(row[i])) has_nan = 1;
+      else if (row[i] > m) m = row[i];
+    }
+    if (has_nan) m = NAN;
+    for (i = 0; i < cols; i++) {
+      float d = row[i] - m;
+      p[r * cols + i] = mxref_exp(d);
+    }
+  }
+  return 0;
+}
+
+int mxref_softmax_quantize(int fmt, int block, const float *s, int64_t rows,
+                           int64_t cols, uint8_t *codes, uint8_t *scales) {
+  const fmt_t *f = get_fmt(fmt);
+  int64_t r, j, nbr;
+  double v[BLOCK];
+  int c[BLOCK], k;
+  float prow[BLOCK];
+  if (check_args(fmt, block, rows, cols) || fmt == MXREF_AXS6) return -1;
+  nbr = cols / BLOCK;
+  for (r = 0; r < rows; r++) {
+    const float *row = s + r * cols;
+    float m = -INFINITY;
+    int has_nan = 0;
+    int64_t i;
+    for (i = 0; i < cols; i++) {
+      if (isnan(row[i])) has_nan = 1;
+      else if (row[i] > m) m = row[i];
+    }
+    if (has_nan) m = NAN;
+    for (j = 0; j < nbr; j++) {
+      int64_t b = r * nbr + j;
+      for (k = 0; k < BLOCK; k++) {
+        float d = row[j * BLOCK + k] - m;
+        prow[k] = mxref_exp(d);
+        v[k] = (double)prow[k];
+      }
+      scales[b] = (uint8_t)quantize_values(f, fmt, v, c);
+      pack_block(f, c, codes + b * f->bpb);
+    }
+  }
+  return 0;
+}
