@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of MX quantize+pack on one MI355X.
+
+Headline: a bf16 linear weight [14336, 4096] (N(0, 0.02^2), seed 3) quantized
+to packed MXFP6 E2M3 with one E8M0 scale per 32 values.  One step = one
+mx_quantize call over the whole tensor; inputs and outputs rotate over enough
+buffer sets (>= 1 GiB in total) that no set is still in the 256 MB last-level
+cache when it is reused, and everything is resident in HBM before timing.
+
+Prints ONE JSON line.  value = GB/s of bf16 input consumed (1 GB = 1e9 B);
+roofline.achieved = algorithmic bytes (input + codes + scales) per launch over
+the measured average launch time, against the 8 TB/s HBM peak.  The other
+steps of the path (E3M2, dequantize, AXS-6 fake-quantize, exp-then-quantize
+probabilities, dynamic activations) are timed the same way and reported under
+"secondary".  cpu_baseline times the CPU oracle on a bounded row sample of the
+same input, and the same rows are compared byte for byte with the GPU output.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak, GB/s
+CACHE_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30
+METRIC = "MX quantize+pack GB/s and % of HBM peak, bf16 14336×4096 → MXFP6 E2M3"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def rotation_sets(bytes_per_set: int) -> int:
+    return max(2, -(-ROTATE_BYTES // bytes_per_set))
+
+
+def time_launches(fn, nsets, steps, warmup):
+    """Average device time per launch (ms) over `steps` back-to-back launches,
+    measured with HIP events on the stream the launches go to."""
+    import torch
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(i % nsets)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bf16_dev(bits_np, copies):
+    import numpy as np
+    import torch
+    base = torch.from_numpy(np.ascontiguousarray(bits_np).view(np.int16)).view(torch.bfloat16).cuda()
+    return [base] + [base.clone() for _ in range(copies - 1)]
+
+
+def headline(mx, x_np, steps, warmup):
+    import torch
+    rows, cols = x_np.shape
+    nb = rows * cols // 32
+    in_bytes = rows * cols * 2
+    out_bytes = nb * 24 + nb
+    nsets = rotation_sets(in_bytes + out_bytes)
+    xs = bf16_dev(x_np, nsets)
+    codes = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    scales = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        st = mx.mx_quantize(0, 32, mx.MX_BF16, xs[i], rows, cols, codes[i], scales[i], None, stream)
+        if st:
+            raise mx.MxError(st, "mx_quantize")
+
+    ms = time_launches(step, nsets, steps, warmup)
+    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0]
+
+
+def secondary(mx, steps):
+    """Other steps of the path, each at its workload's full size."""
+    import numpy as np
+    import torch
+    from block_scaled_bit_amd import workloads
+    res = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    k = max(10, steps // 4)
+
+    def record(name, ms, in_b, out_b, note):
+        res[name] = {"us": round(ms * 1e3, 2), "input_GBps": round(in_b / ms / 1e6, 1),
+                     "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "bytes": in_b + out_b, "workload": note}
+
+    # linear weight: E3M2 quantize, E2M3 and E3M2 dequantize to bf16
+    w = workloads.linear_weight()
+    rows, cols = w.shape
+    nb = rows * cols // 32
+    n = rotation_sets(rows * cols * 2 + nb * 25)
+    xs = bf16_dev(w, n)
+    cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    for f, nm in ((1, "e3m2"), (0, "e2m3")):
+        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3)
+        if f == 1:
+            record("quantize_e3m2", ms, rows * cols * 2, nb * 25, "linear_weight bf16 14336x4096")
+        ms = time_launches(lambda i: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+        record(f"dequantize_{nm}_to_bf16", ms, nb * 25, rows * cols * 2, "linear_weight bf16 14336x4096")
+    del xs, cs, ss
+
+    # AXS-6 weight: fake-quantize and quantize
+    a = workloads.axs6_weight()
+    rows, cols = a.shape
+    nb = rows * cols // 32
+    n = rotation_sets(rows * cols * 4)
+    xs = bf16_dev(a, n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
+    ms = time_launches(lambda i: mx.mx_fake_quantize(4, 32, 0, xs[i], ys[i], rows, cols, stream), n, k, 3)
+    record("fake_quantize_axs6", ms, rows * cols * 2, rows * cols * 2, "axs6_weight bf16 4096x4096")
+    cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    aa = [torch.empty((nb + 3) // 4, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ms = time_launches(lambda i: mx.mx_quantize(4, 32, 0, xs[i], rows, cols, cs[i], ss[i], aa[i], stream), n, k, 3)
+    record("quantize_axs6", ms, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, "axs6_weight bf16 4096x4096")
+    del xs, ys, cs, ss, aa
+
+    # dynamic activations: E4M3 and E2M3 quantize, E4M3 dequantize
+    act = workloads.activations()
+    rows, cols = act.shape
+    nb = rows * cols // 32
+    n = rotation_sets(rows * cols * 2 + nb * 33)
+    xs = bf16_dev(act, n)
+    cs = [torch.empty(nb * 32, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    for f, nm, bpb in ((3, "e4m3", 32), (0, "e2m3", 24)):
+        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3)
+        record(f"quantize_{nm}_activations", ms, rows * cols * 2, nb * (bpb + 1), "activations bf16 16384x8192")
+    ms = time_launches(lambda i: mx.mx_dequantize(3, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+    record("dequantize_e4m3_activations", ms, nb * 33, rows * cols * 2, "activations bf16 16384x8192")
+    del xs, cs, ss
+
+    # attention probabilities: exp-then-quantize to E2M1 (2 GiB of scores)
+    s = workloads.attn_scores()
+    rows, cols = s.shape
+    nb = rows * cols // 32
+    sd = torch.from_numpy(s).cuda()
+    del s
+    c = torch.empty(nb * 16, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ms = time_launches(lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream), 1, max(5, k // 4), 2)
+    record("softmax_quantize_e2m1", ms, rows * cols * 4, nb * 17, "attn_scores fp32 32x4096x4096")
+    ms = time_launches(lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, 1, sd, stream), 1, max(5, k // 4), 2)
+    record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
+    del sd, c, sc
+
+    # small fp32 tensor: latency of the three ops
+    xsm = torch.from_numpy(workloads.weights_small()).cuda()
+    cc = torch.empty(1024 * 24, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    yy = torch.empty_like(xsm)
+    ms = time_launches(lambda i: mx.mx_quantize(0, 32, 1, xsm, 128, 256, cc, s1, None, stream), 1, k, 3)
+    record("quantize_e2m3_weights_small", ms, 131072, 25600, "weights_small fp32 128x256 (launch-bound)")
+    return res
+
+
+def cpu_baseline(x_np, gpu_codes, gpu_scales, budget_s=12.0):
+    """The CPU oracle, as it stands, on a bounded sample of rows (T threads,
+    one contiguous row range each); the same rows are compared with the GPU."""
+    import numpy as np
+
+    import oracle
+    rows, cols = x_np.shape
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    probe = 64
+    t = time.perf_counter()
+    oracle.quantize(0, x_np[:probe])
+    rate = probe / (time.perf_counter() - t)  # rows per second per thread
+    nrows = int(min(rows, max(threads, rate * threads * budget_s)))
+    nrows -= nrows % threads
+    chunk = nrows // threads
+    sample = x_np[:nrows]
+    t = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda i: oracle.quantize(0, sample[i * chunk:(i + 1) * chunk]),
+                            range(threads)))
+    wall = time.perf_counter() - t
+    oc = np.concatenate([p[0] for p in parts])
+    os_ = np.concatenate([p[1] for p in parts])
+    nb = nrows * cols // 32
+    g_codes = gpu_codes[: nb * 24].cpu().numpy().reshape(oc.shape)
+    g_scales = gpu_scales[:nb].cpu().numpy().reshape(os_.shape)
+    parity = bool(np.array_equal(g_codes, oc) and np.array_equal(g_scales, os_))
+    value = nrows * cols * 2 / wall / 1e9
+    base = {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nrows} of {rows} rows of the same bf16 input "
+                      f"({nrows * cols} values), E2M3 quantize+pack, {threads} threads x "
+                      f"{chunk} rows, {wall:.1f} s wall"}
+    return base, parity, nrows
+
+
+def traffic_for(digest):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(steps):
+    """A plain device copy of the headline's byte count (for counter scaling)."""
+    import torch
+    n = 163315712
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
+    b = torch.empty_like(a)
+    ms = time_launches(lambda i: b.copy_(a), 1, steps, 3)
+    print(json.dumps({"copy_bytes_each_way": n, "us": round(ms * 1e3, 2),
+                      "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true", help="time only the headline kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only time a plain device copy of the headline's byte count")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the quantizer shards by rows with no exchange, so "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not run here; use --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_bit_amd as mx
+    from block_scaled_bit_amd import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    x = workloads.linear_weight()
+    ms, in_b, alg_b, nsets, codes0, scales0 = headline(mx, x, args.steps, args.warmup)
+    achieved = alg_b / ms / 1e6
+    digest = source_digest()
+    out = {
+        "metric": METRIC,
+        "value": round(in_b / ms / 1e6, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "linear_weight bf16 14336x4096 -> MXFP6 E2M3 quantize+pack",
+                   "rows": 14336, "cols": 4096, "block": 32, "format": "mxfp6_e2m3",
+                   "input_dtype": "bf16", "rotation_sets": nsets,
+                   "algorithmic_bytes_per_pass": alg_b, "source_digest": digest},
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(digest)},
+    }
+    if not args.no_cpu_baseline:
+        base, parity, nrows = cpu_baseline(x, codes0, scales0)
+        out["cpu_baseline"] = base
+        out["parity"] = {"bit_exact": parity, "rows_compared": nrows}
+    if not args.no_secondary:
+        del codes0, scales0
+        torch.cuda.empty_cache()
+        out["secondary"] = secondary(mx, args.steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

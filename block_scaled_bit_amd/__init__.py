@@ -1,0 +1,201 @@
+"""Python binding of libmx.so: block-shared-exponent quantization on gfx950.
+
+The functions named ``mx_*`` mirror the C ABI of ``include/mx.h`` one for one
+(argument marshalling only: torch tensors become device pointers, the
+current torch stream becomes the HIP stream).  ``quantize``, ``dequantize``,
+``fake_quantize`` and ``softmax_quantize`` additionally allocate their
+outputs with torch.  All arithmetic runs in the HIP kernels; if the library
+is not built this module raises at import time instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
+
+__all__ = [
+    "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
+    "FORMATS", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
+    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "quantize", "dequantize",
+    "fake_quantize", "softmax_quantize", "library_path",
+]
+
+MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3, MX_AXS6 = 0, 1, 2, 3, 4
+MX_BF16, MX_FP32 = 0, 1
+BLOCK = 32
+BYTES_PER_BLOCK = {0: 24, 1: 24, 2: 16, 3: 32, 4: 24}
+# format names used by the pages' configuration strings
+FORMATS = {"mxfp6": MX_FP6_E2M3, "mxfp6_e2m3": MX_FP6_E2M3, "mxfp6_e3m2": MX_FP6_E3M2,
+           "mxfp4": MX_FP4_E2M1, "mxfp8": MX_FP8_E4M3, "axs6": MX_AXS6}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmx.so")
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mx_status_str(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build the HIP library first "
+            "(python -m block_scaled_bit_amd.build)")
+    lib = ctypes.CDLL(library_path)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.mx_abi_version.restype = I
+    lib.mx_status_str.argtypes = [I]
+    lib.mx_status_str.restype = ctypes.c_char_p
+    lib.mx_buffer_sizes.argtypes = [I, I, I64, I64, P, P, P]
+    lib.mx_quantize.argtypes = [I, I, I, P, I64, I64, P, P, P, P]
+    lib.mx_dequantize.argtypes = [I, I, P, P, P, I64, I64, I, P, P]
+    lib.mx_fake_quantize.argtypes = [I, I, I, P, P, I64, I64, P]
+    lib.mx_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P, P]
+    for f in ("mx_buffer_sizes", "mx_quantize", "mx_dequantize", "mx_fake_quantize",
+              "mx_softmax_quantize"):
+        getattr(lib, f).restype = I
+    return lib
+
+
+_lib = _load()
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def _ptr(t) -> int | None:
+    """Device address of a tensor, an int address, or None (NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MxError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# one-for-one C ABI
+# ---------------------------------------------------------------------------
+def mx_abi_version() -> int:
+    return _lib.mx_abi_version()
+
+
+def mx_status_str(status: int) -> str:
+    return _lib.mx_status_str(int(status)).decode()
+
+
+def mx_buffer_sizes(fmt, block: int, rows: int, cols: int):
+    c, s, a = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.mx_buffer_sizes(_fmt(fmt), block, rows, cols, ctypes.byref(c), ctypes.byref(s),
+                                ctypes.byref(a)), "mx_buffer_sizes")
+    return c.value, s.value, a.value
+
+
+def mx_quantize(fmt, block, in_dtype, x, rows, cols, codes, scales, aux, stream=None) -> int:
+    return _lib.mx_quantize(_fmt(fmt), block, in_dtype, _ptr(x), rows, cols, _ptr(codes),
+                            _ptr(scales), _ptr(aux), _stream(stream))
+
+
+def mx_dequantize(fmt, block, codes, scales, aux, rows, cols, out_dtype, y, stream=None) -> int:
+    return _lib.mx_dequantize(_fmt(fmt), block, _ptr(codes), _ptr(scales), _ptr(aux), rows, cols,
+                              out_dtype, _ptr(y), _stream(stream))
+
+
+def mx_fake_quantize(fmt, block, dtype, x, y, rows, cols, stream=None) -> int:
+    return _lib.mx_fake_quantize(_fmt(fmt), block, dtype, _ptr(x), _ptr(y), rows, cols,
+                                 _stream(stream))
+
+
+def mx_softmax_quantize(fmt, block, s, rows, cols, codes, scales, stream=None) -> int:
+    return _lib.mx_softmax_quantize(_fmt(fmt), block, _ptr(s), rows, cols, _ptr(codes),
+                                    _ptr(scales), _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# tensor-level helpers (allocate outputs with torch)
+# ---------------------------------------------------------------------------
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    if t.dtype == torch.float32:
+        return MX_FP32
+    raise MxError(4, f"dtype {t.dtype}")
+
+
+def _rows_cols(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensor must be in GPU memory (the kernels read device pointers)")
+    if t.dim() == 0:
+        raise ValueError("tensor needs at least one dimension")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    cols = t.shape[-1]
+    return (t.numel() // cols if cols else 0), cols
+
+
+def quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK):
+    """Returns (codes uint8 [.., cols/32, bpb], scales uint8 [.., cols/32],
+    aux uint8 [ceil(nblocks/4)] (AXS-6) or None)."""
+    f = _fmt(fmt)
+    rows, cols = _rows_cols(x)
+    nbr = cols // BLOCK if cols % BLOCK == 0 else 0
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=x.device)
+    aux = (torch.empty(((rows * nbr) + 3) // 4, dtype=torch.uint8, device=x.device)
+           if f == MX_AXS6 else None)
+    _check(mx_quantize(f, block, _dtype_code(x), x, rows, cols, codes, scales, aux), "mx_quantize")
+    return codes, scales, aux
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, aux=None, fmt="mxfp6_e2m3",
+               out_dtype=torch.bfloat16, block: int = BLOCK):
+    f = _fmt(fmt)
+    if not (codes.is_cuda and scales.is_cuda):
+        raise ValueError("codes and scales must be in GPU memory")
+    lead = tuple(scales.shape[:-1])
+    cols = scales.shape[-1] * BLOCK
+    rows = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
+    y = torch.empty(lead + (cols,), dtype=out_dtype, device=codes.device)
+    _check(mx_dequantize(f, block, codes, scales, aux, rows, cols, _dtype_code(y), y),
+           "mx_dequantize")
+    return y
+
+
+def fake_quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK, out=None):
+    """Fused quantize->dequantize in x's dtype (out=x works in place)."""
+    f = _fmt(fmt)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    _check(mx_fake_quantize(f, block, _dtype_code(x), x, y, rows, cols), "mx_fake_quantize")
+    return y
+
+
+def softmax_quantize(s: torch.Tensor, fmt="mxfp4", block: int = BLOCK):
+    """P = exp(s - rowmax) per row, then block quantization of P."""
+    f = _fmt(fmt)
+    if s.dtype != torch.float32:
+        raise MxError(4, "softmax_quantize needs fp32 scores")
+    rows, cols = _rows_cols(s)
+    nbr = cols // BLOCK if cols % BLOCK == 0 else 0
+    lead = tuple(s.shape[:-1])
+    codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=s.device)
+    scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=s.device)
+    _check(mx_softmax_quantize(f, block, s, rows, cols, codes, scales), "mx_softmax_quantize")
+    return codes, scales

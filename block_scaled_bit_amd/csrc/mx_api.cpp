@@ -1,0 +1,117 @@
+// mx_api.cpp -- the C ABI declared in include/mx.h: host-side validation and
+// dispatch to the gfx950 kernels.  Nothing here allocates or keeps state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx.h"
+#include "mx_kernels.h"
+
+namespace {
+
+constexpr int kBytesPerBlock[5] = {24, 24, 16, 32, 24};
+
+bool fmt_ok(int f) { return f >= MX_FP6_E2M3 && f <= MX_AXS6; }
+bool dtype_ok(int d) { return d == MX_BF16 || d == MX_FP32; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common shape / format checks.  Sets *nothing = true for an empty tensor.
+mx_status check_common(int fmt, int block, int64_t rows, int64_t cols, bool* nothing) {
+  if (!fmt_ok(fmt)) return MX_ERR_UNSUPPORTED;
+  if (block != MX_BLOCK) return MX_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  if (cols % MX_BLOCK != 0) return MX_ERR_SHAPE;
+  // the element count must fit the byte offsets the kernels form
+  if (rows > 0 && cols > 0 && rows > (INT64_MAX / 8) / cols) return MX_ERR_SHAPE;
+  *nothing = (rows == 0 || cols == 0);
+  return MX_OK;
+}
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MX_ABI_VERSION; }
+
+const char* mx_status_str(int status) {
+  switch (status) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL";
+    case MX_ERR_SHAPE: return "bad shape: rows/cols must be >= 0 and cols a multiple of 32";
+    case MX_ERR_ALIGN: return "x, y and codes must be 16-byte aligned";
+    case MX_ERR_UNSUPPORTED: return "unsupported format, dtype or block size (block must be 32)";
+    case MX_ERR_DEVICE: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
+                          size_t* code_bytes, size_t* scale_bytes, size_t* aux_bytes) {
+  bool nothing = false;
+  mx_status st = check_common(fmt, block, rows, cols, &nothing);
+  if (st != MX_OK) return st;
+  const int64_t nb = nothing ? 0 : rows * (cols / MX_BLOCK);
+  if (code_bytes) *code_bytes = (size_t)nb * (size_t)kBytesPerBlock[fmt];
+  if (scale_bytes) *scale_bytes = (size_t)nb;
+  if (aux_bytes) *aux_bytes = (fmt == MX_AXS6) ? (size_t)((nb + 3) / 4) : 0u;
+  return MX_OK;
+}
+
+mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype, const void* x, int64_t rows,
+                      int64_t cols, void* codes, uint8_t* scales, uint8_t* aux, void* stream) {
+  bool nothing = false;
+  mx_status st = check_common(fmt, block, rows, cols, &nothing);
+  if (st != MX_OK) return st;
+  if (!dtype_ok(in_dtype)) return MX_ERR_UNSUPPORTED;
+  if (nothing) return MX_OK;
+  if (!x || !codes || !scales || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * (cols / MX_BLOCK);
+  return from_hip(mxk::launch_quantize(fmt, in_dtype == MX_BF16, x, nb, codes, scales, aux,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_dequantize(mx_format fmt, int block, const void* codes, const uint8_t* scales,
+                        const uint8_t* aux, int64_t rows, int64_t cols, mx_dtype out_dtype,
+                        void* y, void* stream) {
+  bool nothing = false;
+  mx_status st = check_common(fmt, block, rows, cols, &nothing);
+  if (st != MX_OK) return st;
+  if (!dtype_ok(out_dtype)) return MX_ERR_UNSUPPORTED;
+  if (nothing) return MX_OK;
+  if (!codes || !scales || !y || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * (cols / MX_BLOCK);
+  return from_hip(mxk::launch_dequantize(fmt, out_dtype == MX_BF16, codes, scales, aux, nb, y,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype, const void* x, void* y,
+                           int64_t rows, int64_t cols, void* stream) {
+  bool nothing = false;
+  mx_status st = check_common(fmt, block, rows, cols, &nothing);
+  if (st != MX_OK) return st;
+  if (!dtype_ok(dtype)) return MX_ERR_UNSUPPORTED;
+  if (nothing) return MX_OK;
+  if (!x || !y) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  const int64_t nb = rows * (cols / MX_BLOCK);
+  return from_hip(mxk::launch_fake_quantize(fmt, dtype == MX_BF16, x, nb, y,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_softmax_quantize(mx_format fmt, int block, const float* s, int64_t rows,
+                              int64_t cols, void* codes, uint8_t* scales, void* stream) {
+  bool nothing = false;
+  mx_status st = check_common(fmt, block, rows, cols, &nothing);
+  if (st != MX_OK) return st;
+  if (fmt == MX_AXS6) return MX_ERR_UNSUPPORTED;
+  if (nothing) return MX_OK;
+  if (!s || !codes || !scales) return MX_ERR_NULL;
+  if (!aligned16(s) || !aligned16(codes)) return MX_ERR_ALIGN;
+  return from_hip(mxk::launch_softmax_quantize(fmt, s, rows, cols, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,21 @@
+// mx_kernels.h -- internal launchers of the gfx950 kernels (not part of the
+// C ABI).  Each enqueues one kernel on `st` and returns hipGetLastError().
+// Formats: 0 E2M3, 1 E3M2, 2 E2M1, 3 E4M3, 4 AXS-6.  nb = number of 32-value
+// blocks.  Arguments are validated by the C-ABI layer before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
+                           uint8_t* scales, uint8_t* aux, hipStream_t st);
+hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
+                             const uint8_t* aux, int64_t nb, void* y, hipStream_t st);
+hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,
+                                hipStream_t st);
+hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
+                                   void* codes, uint8_t* scales, hipStream_t st);
+
+}  // namespace mxk

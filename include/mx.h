@@ -1,0 +1,136 @@
+/*
+ * mx.h -- C ABI of the gfx950 block-shared-exponent quantization library
+ * (libmx.so, built from block_scaled_bit_amd/csrc).
+ *
+ * The method: every block of 32 contiguous values along the last dimension
+ * shares one power-of-two scale chosen from the block's largest magnitude,
+ * and each value is stored as a low-bit element code under that scale.
+ *   - "Online MXFP6" (Sonar feature page), "Start a model": packed six-bit
+ *     data and an E8M0 scale for each block of 32 values; "Select the FP6
+ *     encoding": E2M3 (more mantissa) or E3M2 (larger finite range);
+ *     "Current limits": dense dimensions are multiples of 128, unsupported
+ *     layers stay in BF16.
+ *   - "EFQ-Softmax" explainer, "Jargon" and article: MXFP4 = E2M1 codes
+ *     under one block scale; the scale is exponent-only and comes from the
+ *     block's local maximum; exp-then-quantize probability generation.
+ *   - "AXS-6: Adaptive eXponent Sharing", "Overview": one 8-bit shared
+ *     exponent and a 2-bit config per 32 values, sign + 5-bit mantissa per
+ *     value; "Quick Start": fused_fake_quantize(x, block_size=32).
+ *   - "eXmY" abstract: non-power-of-two bit widths packed with no wasted
+ *     bits while staying byte addressable.
+ *
+ * Rules (identical to the CPU oracle's):
+ *   scale byte  0xFF if the block holds a NaN or an infinity; 0 if every
+ *               value is zero; else clamp(floor(log2 amax) - emax + 127,
+ *               0, 254) with emax = 2 (E2M3, E2M1), 4 (E3M2), 8 (E4M3),
+ *               0 (AXS-6).  Scale X = 2^(byte - 127).
+ *   element     |v| / X clamped to the format's largest finite value
+ *               (7.5, 28, 6, 448, 31/16), rounded to the nearest
+ *               representable value, ties to the even code; sign copied
+ *               (so -0 and tiny negatives give a negative-zero code).  In a
+ *               0xFF block every code is 0.
+ *   packing     codes form a little-endian bit stream per block: code k in
+ *               stream bits [k*w, k*w+w), stream bit s in bit s%8 of byte
+ *               s/8 (6-bit: 4 codes per 3 bytes; 4-bit: even element in the
+ *               low nibble; 8-bit: one code per byte).
+ *   dequantize  sign * value(code) * X, rounded to the output type
+ *               (nearest-even); 0xFF blocks, E4M3 NaN codes and AXS-6
+ *               blocks whose config is not 0 give the canonical quiet NaN
+ *               (bf16 0x7FC0, fp32 0x7FC00000).
+ *
+ * Buffers (caller-owned device memory, contiguous, row-major; nb = rows *
+ * cols / 32 blocks, block b = row * (cols/32) + j):
+ *   x, y     [rows, cols] bf16 or fp32, 16-byte aligned
+ *   codes    [rows, cols/32, bpb] bytes, bpb = 24 (FP6, AXS-6), 16 (FP4),
+ *            32 (FP8); 16-byte aligned
+ *   scales   [rows, cols/32] bytes (E8M0; AXS-6 shared exponent, same
+ *            encoding)
+ *   aux      AXS-6 only: ceil(nb/4) bytes, block b's 2-bit config in bits
+ *            2*(b%4).. of byte b/4; ignored (may be NULL) otherwise
+ *
+ * Conventions: every call is asynchronous on `stream` (a hipStream_t; NULL
+ * is the default stream).  Argument errors are found on the host before
+ * anything is enqueued and returned synchronously; a launch failure returns
+ * MX_ERR_DEVICE.  rows == 0 or cols == 0 is a no-op returning MX_OK.  The
+ * library allocates nothing and keeps no state between calls.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MX_ABI_VERSION 1
+#define MX_BLOCK 32
+
+typedef enum {
+  MX_FP6_E2M3 = 0, /* OCP MXFP6 E2M3 ("mxfp6", "mxfp6_e2m3") */
+  MX_FP6_E3M2 = 1, /* OCP MXFP6 E3M2 ("mxfp6_e3m2") */
+  MX_FP4_E2M1 = 2, /* OCP MXFP4 E2M1 ("mxfp4") */
+  MX_FP8_E4M3 = 3, /* OCP MXFP8 E4M3 ("mxfp8") */
+  MX_AXS6 = 4      /* AXS-6: shared exponent, sign + 5-bit mantissa */
+} mx_format;
+
+typedef enum { MX_BF16 = 0, MX_FP32 = 1 } mx_dtype;
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,        /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,       /* rows/cols negative, or cols % 32 != 0 */
+  MX_ERR_ALIGN = 3,       /* x, y or codes not 16-byte aligned */
+  MX_ERR_UNSUPPORTED = 4, /* format, dtype or block size not supported */
+  MX_ERR_DEVICE = 5       /* the HIP launch failed */
+} mx_status;
+
+/* MX_ABI_VERSION of the built library. */
+int mx_abi_version(void);
+
+/* Static description of a status; never NULL. */
+const char *mx_status_str(int status);
+
+/* Sizes in bytes of the codes, scales and aux buffers for a [rows, cols]
+ * tensor (aux is 0 except for AXS-6).  Any output pointer may be NULL. */
+mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
+                          size_t *code_bytes, size_t *scale_bytes,
+                          size_t *aux_bytes);
+
+/* Quantize + pack ("Online MXFP6", "Start a model": replace a tensor by
+ * packed codes plus one scale per 32 values).  x: [rows, cols] of in_dtype.
+ * Writes codes, scales and (AXS-6) aux; every byte of them is written. */
+mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype,
+                      const void *x, int64_t rows, int64_t cols, void *codes,
+                      uint8_t *scales, uint8_t *aux, void *stream);
+
+/* Dequantize: codes + scales (+ aux) -> y [rows, cols] of out_dtype. */
+mx_status mx_dequantize(mx_format fmt, int block, const void *codes,
+                        const uint8_t *scales, const uint8_t *aux,
+                        int64_t rows, int64_t cols, mx_dtype out_dtype,
+                        void *y, void *stream);
+
+/* Fused fake-quantize ("AXS-6", "Quick Start"): y = dequantize(quantize(x))
+ * in x's dtype, one pass, no packed intermediate.  y == x (in place) is
+ * allowed; other overlaps are not. */
+mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype,
+                           const void *x, void *y, int64_t rows, int64_t cols,
+                           void *stream);
+
+/* Exp-then-quantize attention probabilities ("EFQ-Softmax" explainer,
+ * "Jargon": exp-then-quantize, shifted scores): per row of s [rows, cols]
+ * fp32, m = the row maximum (NaN if the row holds a NaN), d = s - m in
+ * fp32, P = exp(d) evaluated in fp32 by Cody-Waite reduction n = rint(d *
+ * log2 e), r = d - n ln2 (two fused multiply-adds with a 16-bit-head split
+ * of ln2), a degree-7 Taylor polynomial by Horner's rule with fused
+ * multiply-adds, times 2^n; then P is quantized exactly as mx_quantize
+ * would quantize it as fp32 input.  fmt: any MX format (not AXS-6). */
+mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
+                              int64_t rows, int64_t cols, void *codes,
+                              uint8_t *scales, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/mx.h
+declares, and rejects bad arguments before anything reaches a GPU (these
+calls pass fake pointers and the NULL stream; none of them launches)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import block_scaled_bit_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("mx_quantize", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize",
+              "mx_buffer_sizes", "mx_status_str", "mx_abi_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(mx):
+    out = subprocess.run(["nm", "-D", "--defined-only", mx.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mx_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(mx.library_path)
+    for f in declared_functions():
+        assert getattr(lib, f) is not None
+
+
+def test_library_is_gfx950_only(mx):
+    # the offload targets named in the embedded code objects (our own build)
+    data = open(mx.library_path, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_version_and_status_strings(mx):
+    assert mx.mx_abi_version() == 1
+    for s in range(0, 7):
+        assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
+
+
+@pytest.mark.parametrize("fmt,code,scale,aux", [(0, 24, 1, 0), (1, 24, 1, 0), (2, 16, 1, 0),
+                                                (3, 32, 1, 0), (4, 24, 1, 1)])
+def test_buffer_sizes(mx, fmt, code, scale, aux):
+    rows, cols = 14336, 4096
+    nb = rows * cols // 32
+    c, s, a = mx.mx_buffer_sizes(fmt, 32, rows, cols)
+    assert (c, s) == (nb * code, nb * scale)
+    assert a == ((nb + 3) // 4 if aux else 0)
+    assert mx.mx_buffer_sizes(fmt, 32, 0, 4096) == (0, 0, 0)
+
+
+S, OK, NULL, SHAPE, ALIGN, UNSUP = None, 0, 1, 2, 3, 4
+A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 32, 0, A, 4, 33, A, A, None), SHAPE),        # cols not a multiple of 32
+    ((0, 32, 0, A, -1, 32, A, A, None), SHAPE),       # negative rows
+    ((0, 16, 0, A, 4, 32, A, A, None), UNSUP),        # block size
+    ((5, 32, 0, A, 4, 32, A, A, None), UNSUP),        # format
+    ((0, 32, 2, A, 4, 32, A, A, None), UNSUP),        # dtype
+    ((0, 32, 0, None, 4, 32, A, A, None), NULL),      # x
+    ((0, 32, 0, A, 4, 32, None, A, None), NULL),      # codes
+    ((0, 32, 0, A, 4, 32, A, None, None), NULL),      # scales
+    ((4, 32, 0, A, 4, 32, A, A, None), NULL),         # AXS-6 needs aux
+    ((0, 32, 0, A + 8, 4, 32, A, A, None), ALIGN),    # x misaligned
+    ((0, 32, 0, A, 4, 32, A + 4, A, None), ALIGN),    # codes misaligned
+    ((0, 32, 0, None, 0, 32, None, None, None), OK),  # empty: no-op
+    ((0, 32, 0, None, 5, 0, None, None, None), OK),   # empty: no-op
+])
+def test_quantize_argument_errors(mx, args, want):
+    assert mx.mx_quantize(*args, stream=0) == want
+
+
+def test_other_entry_points_argument_errors(mx):
+    assert mx.mx_dequantize(0, 32, A, A, None, 4, 31, 0, A, stream=0) == SHAPE
+    assert mx.mx_dequantize(0, 32, A, A, None, 4, 32, 7, A, stream=0) == UNSUP
+    assert mx.mx_dequantize(0, 32, A, A, None, 4, 32, 0, None, stream=0) == NULL
+    assert mx.mx_dequantize(4, 32, A, A, None, 4, 32, 0, A, stream=0) == NULL
+    assert mx.mx_dequantize(0, 32, A + 1, A, None, 4, 32, 0, A, stream=0) == ALIGN
+    assert mx.mx_fake_quantize(0, 32, 0, A, None, 4, 32, stream=0) == NULL
+    assert mx.mx_fake_quantize(0, 32, 0, A, A + 2, 4, 32, stream=0) == ALIGN
+    assert mx.mx_fake_quantize(0, 8, 0, A, A, 4, 32, stream=0) == UNSUP
+    assert mx.mx_softmax_quantize(4, 32, A, 4, 32, A, A, stream=0) == UNSUP
+    assert mx.mx_softmax_quantize(2, 32, A, 4, 30, A, A, stream=0) == SHAPE
+    assert mx.mx_softmax_quantize(2, 32, None, 4, 32, A, A, stream=0) == NULL
+    assert mx.mx_softmax_quantize(2, 32, None, 0, 32, None, None, stream=0) == OK
+
+
+def test_python_helpers_reject_host_tensors(mx):
+    import torch
+    with pytest.raises(ValueError):
+        mx.quantize(torch.zeros(2, 64), "mxfp6")
+    with pytest.raises(ValueError):
+        mx.fake_quantize(torch.zeros(2, 64), "axs6")
+    assert mx.FORMATS["mxfp6"] == mx.MX_FP6_E2M3 and mx.FORMATS["mxfp8"] == mx.MX_FP8_E4M3

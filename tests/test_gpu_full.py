@@ -1,0 +1,141 @@
+"""The five workloads at full size, in the launch configuration the benchmark
+times: GPU results compared with the oracle on sampled rows (blocks run along
+rows, so the oracle on a subset of rows computes exactly those rows' blocks)
+and checked against properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_bit_amd import workloads
+from gpu_util import assert_bytes_equal, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+BPB = oracle.BYTES_PER_BLOCK
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_scaled_bit_amd as m
+    return m
+
+
+def _sample_rows(nrows, k, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(nrows, size=min(k, nrows), replace=False).tolist())
+    rows |= {0, nrows - 1}
+    rows |= set(int(r) for r in extra)
+    return np.array(sorted(rows))
+
+
+def _check_rows(fmt, x_host, rows, gc, gs, ga=None):
+    oc, os_, oa = oracle.quantize(fmt, x_host[rows])
+    assert_bytes_equal(gs[rows], os_, "scales")
+    assert_bytes_equal(gc[rows], oc, "codes", BPB[fmt])
+
+
+def test_weights_small_e2m3_all_ops(mx):
+    x = workloads.weights_small()
+    xd = to_dev(x)
+    codes, scales, _ = mx.quantize(xd, "mxfp6_e2m3")
+    y = mx.dequantize(codes, scales, None, "mxfp6_e2m3", torch.float32)
+    fq = mx.fake_quantize(xd, "mxfp6_e2m3")
+    torch.cuda.synchronize()
+    oc, os_, _ = oracle.quantize(0, x)
+    assert_bytes_equal(to_host(scales), os_, "scales")
+    assert_bytes_equal(to_host(codes), oc, "codes", 24)
+    assert_bytes_equal(to_host(y), oracle.dequantize(0, oc, os_, None, 128, 256, oracle.FP32), "dequant")
+    assert_bytes_equal(to_host(fq), oracle.fake_quantize(0, x), "fake-quant")
+
+
+def test_axs6_weight_fake_quant_and_quantize(mx):
+    x = workloads.axs6_weight()
+    xd = to_dev(x)
+    fq = mx.fake_quantize(xd, "axs6")
+    codes, scales, aux = mx.quantize(xd, "axs6")
+    torch.cuda.synchronize()
+    want = oracle.fake_quantize(4, x)
+    assert_bytes_equal(to_host(fq), want, "AXS-6 fake-quant")
+    oc, os_, oa = oracle.quantize(4, x)
+    assert_bytes_equal(to_host(scales), os_, "scales")
+    assert_bytes_equal(to_host(codes), oc, "codes", 24)
+    assert_bytes_equal(to_host(aux), oa, "config plane")
+    # storage: 6.3125 bits per value; per-block error within the grid's bound
+    n = x.size
+    bits = 8 * (codes.numel() + scales.numel()) + 2 * scales.numel()
+    assert bits / n == 6.3125
+    xf = workloads.bf16_bits_to_f32(x).astype(np.float64).reshape(-1, 32)
+    yf = workloads.bf16_bits_to_f32(to_host(fq)).astype(np.float64).reshape(-1, 32)
+    err = np.abs(xf - yf).max(axis=1)
+    amax = np.abs(xf).max(axis=1)
+    E = np.floor(np.log2(amax))
+    sat = amax >= (31.5 / 16) * np.exp2(E)
+    assert np.all(err[~sat] <= np.exp2(E[~sat] - 5))
+    assert np.all(err <= np.exp2(E - 4))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp6_e2m3", "mxfp6_e3m2"])
+def test_linear_weight_fp6_round_trip(mx, fmt):
+    f = mx.FORMATS[fmt]
+    x = workloads.linear_weight()
+    xd = to_dev(x)
+    codes, scales, _ = mx.quantize(xd, fmt)
+    y = mx.dequantize(codes, scales, None, fmt, torch.bfloat16)
+    fq = mx.fake_quantize(xd, fmt)
+    torch.cuda.synchronize()
+    rows = _sample_rows(x.shape[0], 200, 3)
+    gc, gs = to_host(codes), to_host(scales)
+    _check_rows(f, x, rows, gc, gs)
+    oc, os_, _ = oracle.quantize(f, x[rows])
+    want = oracle.dequantize(f, oc, os_, None, len(rows), x.shape[1], oracle.BF16)
+    assert_bytes_equal(to_host(y)[rows], want, "dequant rows")
+    # at full size: dequantize(quantize(x)) == fake_quantize(x), bitwise
+    assert torch.equal(y.view(torch.int16), fq.view(torch.int16))
+
+
+def test_attention_probabilities_e2m1(mx):
+    s = workloads.attn_scores()
+    sd = to_dev(s)
+    codes, scales = mx.softmax_quantize(sd, "mxfp4")
+    p = mx.dequantize(codes, scales, None, "mxfp4", torch.float32)
+    torch.cuda.synchronize()
+    rows = _sample_rows(s.shape[0], 48, 4)
+    oc, os_ = oracle.softmax_quantize(2, s[rows])
+    gc, gs = to_host(codes), to_host(scales)
+    assert_bytes_equal(gs[rows], os_, "scales")
+    assert_bytes_equal(gc[rows], oc, "codes", 16)
+    want_p = oracle.dequantize(2, oc, os_, None, len(rows), s.shape[1], oracle.FP32)
+    assert_bytes_equal(to_host(p)[rows], want_p, "dequantized P")
+    # full size: no sign bit set; the block holding each row's max has byte 125
+    sign_bits = (codes & 0x88).any()
+    assert not bool(sign_bits)
+    amax_blk = sd.view(sd.shape[0], -1, 32).amax(dim=2).argmax(dim=1)
+    top = scales.gather(1, amax_blk[:, None])
+    assert bool((top == 125).all()) and int(scales.max()) == 125
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp6_e2m3"])
+def test_activations_dynamic_round_trip(mx, fmt):
+    f = mx.FORMATS[fmt]
+    x = workloads.activations()
+    xd = to_dev(x)
+    codes, scales, _ = mx.quantize(xd, fmt)
+    y = mx.dequantize(codes, scales, None, fmt, torch.bfloat16)
+    fq = mx.fake_quantize(xd, fmt)
+    torch.cuda.synchronize()
+    gc, gs = to_host(codes), to_host(scales)
+    with np.errstate(invalid="ignore"):
+        xf = workloads.bf16_bits_to_f32(x)
+    bad_rows = np.nonzero(~np.isfinite(xf).all(axis=1))[0][:40]
+    rows = _sample_rows(x.shape[0], 150, 5, extra=bad_rows)
+    _check_rows(f, x, rows, gc, gs)
+    # full size: a block is poisoned exactly when it holds an inf or a NaN
+    nonfinite = ~np.isfinite(xf.reshape(x.shape[0], -1, 32)).all(axis=2)
+    assert np.array_equal(gs == 0xFF, nonfinite)
+    assert 13000 <= int(nonfinite.sum()) <= 13422
+    zero = (xf.reshape(x.shape[0], -1, 32) == 0).all(axis=2)
+    assert np.all(gs[zero] == 0) and zero.sum() >= 41943
+    assert torch.equal(y.view(torch.int16), fq.view(torch.int16))
