@@ -137,5 +137,6 @@ def test_activations_dynamic_round_trip(mx, fmt):
     assert np.array_equal(gs == 0xFF, nonfinite)
     assert 13000 <= int(nonfinite.sum()) <= 13422
     zero = (xf.reshape(x.shape[0], -1, 32) == 0).all(axis=2)
-    assert np.all(gs[zero] == 0) and zero.sum() >= 41943
+    # 41943 blocks were zeroed; a few of them later received an inf or a NaN
+    assert np.all(gs[zero] == 0) and 41943 - 13422 <= zero.sum() <= 41943 + 100
     assert torch.equal(y.view(torch.int16), fq.view(torch.int16))
