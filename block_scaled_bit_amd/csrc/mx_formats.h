@@ -71,45 +71,29 @@ __device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Rounding of one scaled magnitude a (fp32, a >= 0, already clamped to MAXF)
-// to the nearest grid value, ties to even.  The step at a is
-// 2^(max(floor(log2 a), EMIN) - M); adding C = 2^(that exponent + 23) makes
-// the fp32 adder's own round-to-nearest-even land on that step, because the
-// sum lies in [C, 2C) whose ulp is exactly the step.  Then
-//   n    = bits(a + C) - bits(C)          (multiples of the step)
-//   code = n + (binade - EMIN) << M       (field/mantissa carry included)
-//   r    = (a + C) - C                    (the rounded value, exact)
-// a must be exact: it is |v| * 2^(127 - byte), exact unless it is below
-// 2^-126, where every format rounds it to zero anyway.
+// AXS-6 rounding in software (there is no hardware AXS-6 format): the scaled
+// magnitude a = |v| * 2^(127 - byte) is exact (fp32 ldexp of a bf16/fp32
+// value; only values far below the grid's half step can lose bits, and they
+// round to zero either way), clamped to 31/16, and m = rint(16 a) rounds to
+// nearest even on the 1/16 grid.
 // ---------------------------------------------------------------------------
 struct Rounded {
-  uint32_t mag;  // magnitude code
-  float val;     // rounded magnitude in units of the block scale
+  uint32_t mag;  // magnitude code m
+  float val;     // m / 16, the rounded magnitude in units of the block scale
 };
 
 template <int F>
 __device__ __forceinline__ Rounded round_scaled(float a) {
-  using T = Fmt<F>;
+  static_assert(Fmt<F>::FIXED, "software rounding is used for AXS-6 only");
   Rounded out;
-  if constexpr (T::FIXED) {
-    float m = __builtin_rintf(a * 16.0f);  // a * 16 is exact; RNE
-    m = fminf(m, 31.0f);
-    out.mag = (uint32_t)m;
-    out.val = m * 0.0625f;
-  } else {
-    uint32_t ab = __float_as_uint(a);
-    int ea = (int)(ab >> 23);
-    int et = ea > 127 + T::EMIN ? ea : 127 + T::EMIN;
-    float C = __uint_as_float((uint32_t)(et + 23 - T::M) << 23);
-    float s = a + C;
-    uint32_t n = __float_as_uint(s) - __float_as_uint(C);
-    out.mag = n + ((uint32_t)(et - 127 - T::EMIN) << T::M);
-    out.val = s - C;
-  }
+  float m = __builtin_rintf(a * 16.0f);  // a * 16 is exact; RNE
+  m = fminf(m, 31.0f);
+  out.mag = (uint32_t)m;
+  out.val = m * 0.0625f;
   return out;
 }
 
-// Scaled magnitude of one input value (fp32 bit pattern).
+// Scaled, clamped magnitude of one input value (fp32 bit pattern).
 template <int F>
 __device__ __forceinline__ float scaled_abs(uint32_t vbits, int neg_exp) {
   float av = __uint_as_float(vbits & 0x7FFFFFFFu);
@@ -117,20 +101,11 @@ __device__ __forceinline__ float scaled_abs(uint32_t vbits, int neg_exp) {
   return fminf(a, Fmt<F>::MAXF);
 }
 
-// Unscaled value of a magnitude code (exact in fp32), as significand and
-// exponent so the caller applies the block scale with one ldexp.
+// Unscaled AXS-6 value m/16 times 2^scale_exp (exact in fp32).
 template <int F>
 __device__ __forceinline__ float decode_mag(uint32_t mag, int scale_exp) {
-  using T = Fmt<F>;
-  if constexpr (T::FIXED) {
-    return __builtin_ldexpf((float)mag, scale_exp - 4);
-  } else {
-    uint32_t e = mag >> T::M;
-    uint32_t m = mag & ((1u << T::M) - 1u);
-    uint32_t sig = e ? (m | (1u << T::M)) : m;
-    int ex = (int)(e ? e : 1u) - T::BIAS - T::M;
-    return __builtin_ldexpf((float)sig, ex + scale_exp);
-  }
+  static_assert(Fmt<F>::FIXED, "software decoding is used for AXS-6 only");
+  return __builtin_ldexpf((float)mag, scale_exp - 4);
 }
 
 // fp32 -> bf16 bit pattern, round to nearest even; NaN -> canonical.

@@ -1,10 +1,13 @@
 // mx_kernels.hip -- gfx950 kernels for block-shared-exponent quantization.
 //
-// Generic layout: one lane owns one 32-value block.  The lane reads the
-// block (64 B of bf16 or 128 B of fp32) with 128-bit loads, reduces the
-// largest magnitude in registers, derives the shared scale, rounds every
-// value, and writes its packed codes (24/16/32 B) and its scale byte.  No
-// value crosses lanes, so every output byte has exactly one writer.
+// Layout: one lane owns one 32-value block.  The lane reads its block (64 B
+// of bf16 or 128 B of fp32) with 128-bit loads, reduces the largest
+// magnitude in registers, derives the shared scale byte, converts the 32
+// values with the scaled-convert instructions (FP6: one 32-wide instruction;
+// FP4/FP8: one per pair) or, for AXS-6, with integer/fp32 arithmetic, and
+// writes its packed codes (24/16/32 B) and its scale byte.  No value crosses
+// lanes, so every output byte has exactly one writer and in-place
+// fake-quantization is safe (a lane reads its block before writing it).
 //
 // Rules: "Online MXFP6" page ("Start a model": packed codes and an E8M0
 // scale per 32 values); "EFQ-Softmax" explainer (exponent-only block scale
@@ -14,59 +17,42 @@
 #include <stdint.h>
 
 #include "mx_formats.h"
+#include "mx_hw.h"
 #include "mx_kernels.h"
 
 namespace mxk {
 
+constexpr uint32_t kNaN32 = 0x7FC00000u;
+constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;
+
 // ---------------------------------------------------------------------------
-// Loading one block into 32 fp32 bit patterns.
+// Memory helpers: block b of bf16 is 4 x 16 B at b*64, of fp32 8 x 16 B at
+// b*128; packed codes are W dwords at b*4W.
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__device__ __forceinline__ void load_block(const void* x, int64_t b, uint32_t (&v)[32]) {
-  if constexpr (BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(x) + b * 4;
+__device__ __forceinline__ void load_bf16_block(const void* x, int64_t b, uint32_t (&d)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x) + b * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 q = p[i];
-      uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = w[j] << 16;
-        v[8 * i + 2 * j + 1] = w[j] & 0xFFFF0000u;
-      }
-    }
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(x) + b * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 q = p[i];
-      v[4 * i] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = p[i];
+    d[4 * i] = q.x; d[4 * i + 1] = q.y; d[4 * i + 2] = q.z; d[4 * i + 3] = q.w;
   }
 }
 
-// Storing 32 output values given as fp32 bit patterns (bf16: rounded).
-template <bool BF16>
-__device__ __forceinline__ void store_block(void* y, int64_t b, const uint32_t (&v)[32]) {
-  if constexpr (BF16) {
-    uint4* p = reinterpret_cast<uint4*>(y) + b * 4;
+__device__ __forceinline__ void load_f32_block(const void* x, int64_t b, uint32_t (&d)[32]) {
+  const uint4* p = reinterpret_cast<const uint4*>(x) + b * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = f32_to_bf16_rne(__uint_as_float(v[8 * i + 2 * j])) |
-               (f32_to_bf16_rne(__uint_as_float(v[8 * i + 2 * j + 1])) << 16);
-      p[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  } else {
-    uint4* p = reinterpret_cast<uint4*>(y) + b * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = make_uint4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  for (int i = 0; i < 8; ++i) {
+    const uint4 q = p[i];
+    d[4 * i] = q.x; d[4 * i + 1] = q.y; d[4 * i + 2] = q.z; d[4 * i + 3] = q.w;
   }
+}
+
+template <int N>
+__device__ __forceinline__ void store_dwords16(void* y, int64_t b, const uint32_t (&d)[N]) {
+  static_assert(N % 4 == 0, "whole 16-byte chunks");
+  uint4* p = reinterpret_cast<uint4*>(y) + b * (N / 4);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) p[i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
 }
 
 template <int W>
@@ -76,13 +62,8 @@ __device__ __forceinline__ void store_codes(void* codes, int64_t b, const uint32
     p[0] = make_uint2(o[0], o[1]);
     p[1] = make_uint2(o[2], o[3]);
     p[2] = make_uint2(o[4], o[5]);
-  } else if constexpr (W == 4) {
-    uint4* p = reinterpret_cast<uint4*>(codes) + b;
-    p[0] = make_uint4(o[0], o[1], o[2], o[3]);
   } else {
-    uint4* p = reinterpret_cast<uint4*>(codes) + b * 2;
-    p[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    p[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    store_dwords16<W>(codes, b, o);
   }
 }
 
@@ -92,112 +73,233 @@ __device__ __forceinline__ void load_codes(const void* codes, int64_t b, uint32_
     const uint2* p = reinterpret_cast<const uint2*>(codes) + b * 3;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      uint2 q = p[i];
+      const uint2 q = p[i];
       o[2 * i] = q.x;
       o[2 * i + 1] = q.y;
     }
-  } else if constexpr (W == 4) {
-    uint4 q = reinterpret_cast<const uint4*>(codes)[b];
-    o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(codes) + b * 2;
-    uint4 q0 = p[0], q1 = p[1];
-    o[0] = q0.x; o[1] = q0.y; o[2] = q0.z; o[3] = q0.w;
-    o[4] = q1.x; o[5] = q1.y; o[6] = q1.z; o[7] = q1.w;
+    const uint4* p = reinterpret_cast<const uint4*>(codes) + b * (W / 4);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 q = p[i];
+      o[4 * i] = q.x; o[4 * i + 1] = q.y; o[4 * i + 2] = q.z; o[4 * i + 3] = q.w;
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-// One block in registers: scale byte and codes (the quantize core).
-// ---------------------------------------------------------------------------
-template <int F>
-__device__ __forceinline__ uint32_t quantize_regs(const uint32_t (&v)[32], uint32_t (&c)[32],
-                                                  float (&r)[32]) {
-  using T = Fmt<F>;
-  uint32_t amax = 0u;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) amax = max(amax, v[k] & 0x7FFFFFFFu);
-  const uint32_t byte = scale_byte_from_amax<F>(amax);
-  const int neg_exp = 127 - (int)byte;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    Rounded q = round_scaled<F>(scaled_abs<F>(v[k], neg_exp));
-    const uint32_t sign = v[k] >> 31;
-    c[k] = (byte == 0xFFu) ? 0u : (q.mag | (sign << (T::W - 1)));
-    r[k] = q.val;
-  }
-  return byte;
+// Canonical NaN for every NaN value (fp32 patterns / packed bf16 pairs).
+__device__ __forceinline__ uint32_t canon_nan32(uint32_t u) {
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? kNaN32 : u;
+}
+__device__ __forceinline__ uint32_t canon_nan16x2(uint32_t u) {
+  const uint32_t lo = (u & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (u & 0xFFFFu);
+  const uint32_t hi = ((u >> 16) & 0x7FFFu) > 0x7F80u ? 0x7FC0u : (u >> 16);
+  return lo | (hi << 16);
 }
 
 // ---------------------------------------------------------------------------
-// Kernels
+// MX formats (E2M3, E3M2, E2M1, E4M3): hardware conversions
 // ---------------------------------------------------------------------------
 template <int F, bool BF16>
-__global__ __launch_bounds__(256) void quantize_lpb(const void* __restrict__ x, int64_t nb,
-                                                    void* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales,
-                                                    uint8_t* __restrict__ aux) {
+__global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, int64_t nb,
+                                                   void* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
   constexpr int W = Fmt<F>::W;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-    uint32_t v[32], c[32], o[W];
-    float r[32];
-    load_block<BF16>(x, b, v);
-    const uint32_t byte = quantize_regs<F>(v, c, r);
-    pack32<W>(c, o);
+    uint32_t o[W];
+    uint32_t byte;
+    if constexpr (BF16) {
+      uint32_t d[16];
+      load_bf16_block(x, b, d);
+      byte = scale_byte_from_amax<F>(amax_bf16x32(d));
+      encode_bf16<F>(d, scale_operand(byte), o);
+    } else {
+      uint32_t d[32];
+      load_f32_block(x, b, d);
+      byte = scale_byte_from_amax<F>(amax_f32x32(d));
+      encode_f32<F>(d, scale_operand(byte), o);
+    }
+    if (byte == 0xFFu) {
+#pragma unroll
+      for (int k = 0; k < W; ++k) o[k] = 0u;
+    }
     store_codes<W>(codes, b, o);
     scales[b] = (uint8_t)byte;
-    // AXS-6 config plane: 2 bits per block, all zero (the uniform grid)
-    if constexpr (F == F_AXS6) {
-      if ((b & 3) == 0) aux[b >> 2] = 0;
-    }
   }
 }
 
 template <int F, bool BF16>
-__global__ __launch_bounds__(256) void fake_quantize_lpb(const void* x, int64_t nb, void* y) {
+__global__ __launch_bounds__(256) void dequantize_mx(const void* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     int64_t nb, void* __restrict__ y) {
+  constexpr int W = Fmt<F>::W;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-    uint32_t v[32], c[32], out[32];
-    float r[32];
-    load_block<BF16>(x, b, v);
-    const uint32_t byte = quantize_regs<F>(v, c, r);
-    const int sexp = (int)byte - 127;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float mag = __builtin_ldexpf(r[k], sexp);
-      out[k] = (byte == 0xFFu) ? 0x7FC00000u : (__float_as_uint(mag) | (v[k] & 0x80000000u));
-    }
-    store_block<BF16>(y, b, out);
-  }
-}
-
-template <int F, bool BF16>
-__global__ __launch_bounds__(256) void dequantize_lpb(const void* __restrict__ codes,
-                                                      const uint8_t* __restrict__ scales,
-                                                      const uint8_t* __restrict__ aux, int64_t nb,
-                                                      void* __restrict__ y) {
-  using T = Fmt<F>;
-  constexpr int W = T::W;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-    uint32_t o[W], out[32];
+    uint32_t o[W];
     load_codes<W>(codes, b, o);
     const uint32_t byte = scales[b];
-    bool poisoned = (byte == 0xFFu);
-    if constexpr (F == F_AXS6) poisoned |= ((aux[b >> 2] >> (2 * (b & 3))) & 3u) != 0u;
+    bool fix_nan = (byte == 0xFFu);
+    if constexpr (F == F_E4M3) fix_nan |= e4m3_has_nan_code(o);
+    if constexpr (BF16) {
+      uint32_t d[16];
+      decode_bf16<F>(o, scale_operand(byte), d);
+      if (fix_nan) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) d[k] = (byte == 0xFFu) ? kNaN16x2 : canon_nan16x2(d[k]);
+      }
+      store_dwords16<16>(y, b, d);
+    } else {
+      uint32_t d[32];
+      decode_f32<F>(o, scale_operand(byte), d);
+      if (fix_nan) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) d[k] = (byte == 0xFFu) ? kNaN32 : canon_nan32(d[k]);
+      }
+      store_dwords16<32>(y, b, d);
+    }
+  }
+}
+
+template <int F, bool BF16>
+__global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t nb, void* y) {
+  constexpr int W = Fmt<F>::W;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    uint32_t o[W];
+    if constexpr (BF16) {
+      uint32_t d[16];
+      load_bf16_block(x, b, d);
+      const uint32_t byte = scale_byte_from_amax<F>(amax_bf16x32(d));
+      const float sc = scale_operand(byte);
+      encode_bf16<F>(d, sc, o);
+      decode_bf16<F>(o, sc, d);
+      if (byte == 0xFFu) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) d[k] = kNaN16x2;
+      }
+      store_dwords16<16>(y, b, d);
+    } else {
+      uint32_t d[32];
+      load_f32_block(x, b, d);
+      const uint32_t byte = scale_byte_from_amax<F>(amax_f32x32(d));
+      const float sc = scale_operand(byte);
+      encode_f32<F>(d, sc, o);
+      decode_f32<F>(o, sc, d);
+      if (byte == 0xFFu) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) d[k] = kNaN32;
+      }
+      store_dwords16<32>(y, b, d);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// AXS-6: sign + 5-bit magnitude m, value m/16 under the shared exponent.
+// m = min(rint(|v| * 2^(131 - byte)), 31) in fp32 (exact scaling; RNE).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t axs6_block_byte(const uint32_t (&v)[32]) {
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = max(amax, v[k] & 0x7FFFFFFFu);
+  return scale_byte_from_amax<F_AXS6>(amax);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_values(const void* x, int64_t b, uint32_t (&v)[32]) {
+  if constexpr (BF16) {
+    uint32_t d[16];
+    load_bf16_block(x, b, d);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[2 * k] = d[k] << 16;
+      v[2 * k + 1] = d[k] & 0xFFFF0000u;
+    }
+  } else {
+    load_f32_block(x, b, v);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x, int64_t nb,
+                                                     void* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales,
+                                                     uint8_t* __restrict__ aux) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    uint32_t v[32], c[32], o[6];
+    load_values<BF16>(x, b, v);
+    const uint32_t byte = axs6_block_byte(v);
+    const int neg_exp = 127 - (int)byte;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const Rounded q = round_scaled<F_AXS6>(scaled_abs<F_AXS6>(v[k], neg_exp));
+      c[k] = (byte == 0xFFu) ? 0u : (q.mag | ((v[k] >> 31) << 5));
+    }
+    pack32<6>(c, o);
+    store_codes<6>(codes, b, o);
+    scales[b] = (uint8_t)byte;
+    // config plane: 2 bits per block, all zero (the uniform grid)
+    if ((b & 3) == 0) aux[b >> 2] = 0;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t nb, void* y) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    uint32_t v[32];
+    load_values<BF16>(x, b, v);
+    const uint32_t byte = axs6_block_byte(v);
+    const int neg_exp = 127 - (int)byte, sexp = (int)byte - 127;
+    uint32_t out[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const Rounded q = round_scaled<F_AXS6>(scaled_abs<F_AXS6>(v[k], neg_exp));
+      const float mag = __builtin_ldexpf(q.val, sexp);  // exact
+      out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(mag) | (v[k] & 0x80000000u));
+    }
+    if constexpr (BF16) {
+      // every result is a bf16 value (or the canonical NaN): keep the top half
+      uint32_t d[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) d[k] = (out[2 * k] >> 16) | (out[2 * k + 1] & 0xFFFF0000u);
+      store_dwords16<16>(y, b, d);
+    } else {
+      store_dwords16<32>(y, b, out);
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const uint8_t* __restrict__ aux, int64_t nb,
+                                                       void* __restrict__ y) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    uint32_t o[6], out[32];
+    load_codes<6>(codes, b, o);
+    const uint32_t byte = scales[b];
+    const bool poisoned = (byte == 0xFFu) || (((aux[b >> 2] >> (2 * (b & 3))) & 3u) != 0u);
     const int sexp = (int)byte - 127;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const uint32_t code = unpack1<W>(o, k);
-      const uint32_t mag = code & ((1u << (W - 1)) - 1u);
-      const uint32_t sign = (code >> (W - 1)) << 31;
-      const float val = decode_mag<F>(mag, sexp);
-      bool nan = poisoned;
-      if constexpr (T::NAN_MAG >= 0) nan |= (mag == (uint32_t)T::NAN_MAG);
-      out[k] = nan ? 0x7FC00000u : (__float_as_uint(val) | sign);
+      const uint32_t code = unpack1<6>(o, k);
+      const float val = decode_mag<F_AXS6>(code & 31u, sexp);
+      out[k] = poisoned ? kNaN32 : (__float_as_uint(val) | ((code >> 5) << 31));
     }
-    store_block<BF16>(y, b, out);
+    if constexpr (BF16) {
+      uint32_t d[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        d[k] = f32_to_bf16_rne(__uint_as_float(out[2 * k])) |
+               (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
+      store_dwords16<16>(y, b, d);
+    } else {
+      store_dwords16<32>(y, b, out);
+    }
   }
 }
 
@@ -266,12 +368,12 @@ __global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __rest
   for (int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); row < rows;
        row += waves) {
     const float* srow = s + row * cols;
-    // pass 1: exact row maximum (NaN anywhere makes it NaN)
+    // pass 1: exact row maximum (a NaN anywhere makes it NaN)
     float m = -__builtin_inff();
     int has_nan = 0;
     for (int64_t j = lane; j < nbr; j += 64) {
       uint32_t v[32];
-      load_block<false>(srow, j, v);
+      load_f32_block(srow, j, v);
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         has_nan |= (v[k] & 0x7FFFFFFFu) > 0x7F800000u;
@@ -282,13 +384,16 @@ __global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __rest
     if (wave_or(has_nan)) m = __builtin_nanf("");
     // pass 2: P = exp(s - m), then quantize each block of P
     for (int64_t j = lane; j < nbr; j += 64) {
-      uint32_t v[32], c[32], o[W];
-      float r[32];
-      load_block<false>(srow, j, v);
+      uint32_t v[32], o[W];
+      load_f32_block(srow, j, v);
 #pragma unroll
       for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_fixed(__uint_as_float(v[k]) - m));
-      const uint32_t byte = quantize_regs<F>(v, c, r);
-      pack32<W>(c, o);
+      const uint32_t byte = scale_byte_from_amax<F>(amax_f32x32(v));
+      encode_f32<F>(v, scale_operand(byte), o);
+      if (byte == 0xFFu) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) o[k] = 0u;
+      }
       const int64_t b = row * nbr + j;
       store_codes<W>(codes, b, o);
       scales[b] = (uint8_t)byte;
@@ -306,22 +411,26 @@ static inline dim3 grid_for(int64_t work, int per_wg) {
   return dim3((unsigned)g);
 }
 
-#define MXK_SWITCH_FMT(fmt, BODY)                 \
-  switch (fmt) {                                  \
-    case F_E2M3: { constexpr int FF = F_E2M3; BODY; } break; \
-    case F_E3M2: { constexpr int FF = F_E3M2; BODY; } break; \
-    case F_E2M1: { constexpr int FF = F_E2M1; BODY; } break; \
-    case F_E4M3: { constexpr int FF = F_E4M3; BODY; } break; \
-    case F_AXS6: { constexpr int FF = F_AXS6; BODY; } break; \
-    default: return hipErrorInvalidValue;         \
+#define MXK_SWITCH_MX(fmt, BODY)                                   \
+  switch (fmt) {                                                   \
+    case F_E2M3: { constexpr int FF = F_E2M3; BODY; } break;       \
+    case F_E3M2: { constexpr int FF = F_E3M2; BODY; } break;       \
+    case F_E2M1: { constexpr int FF = F_E2M1; BODY; } break;       \
+    case F_E4M3: { constexpr int FF = F_E4M3; BODY; } break;       \
+    default: return hipErrorInvalidValue;                          \
   }
 
 hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
                            uint8_t* scales, uint8_t* aux, hipStream_t st) {
   const dim3 grid = grid_for(nb, 256), block(256);
-  MXK_SWITCH_FMT(fmt, {
-    if (bf16) hipLaunchKernelGGL((quantize_lpb<FF, true>), grid, block, 0, st, x, nb, codes, scales, aux);
-    else hipLaunchKernelGGL((quantize_lpb<FF, false>), grid, block, 0, st, x, nb, codes, scales, aux);
+  if (fmt == F_AXS6) {
+    if (bf16) hipLaunchKernelGGL(quantize_axs6<true>, grid, block, 0, st, x, nb, codes, scales, aux);
+    else hipLaunchKernelGGL(quantize_axs6<false>, grid, block, 0, st, x, nb, codes, scales, aux);
+    return hipGetLastError();
+  }
+  MXK_SWITCH_MX(fmt, {
+    if (bf16) hipLaunchKernelGGL((quantize_mx<FF, true>), grid, block, 0, st, x, nb, codes, scales);
+    else hipLaunchKernelGGL((quantize_mx<FF, false>), grid, block, 0, st, x, nb, codes, scales);
   });
   return hipGetLastError();
 }
@@ -329,9 +438,14 @@ hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* 
 hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
                              const uint8_t* aux, int64_t nb, void* y, hipStream_t st) {
   const dim3 grid = grid_for(nb, 256), block(256);
-  MXK_SWITCH_FMT(fmt, {
-    if (bf16) hipLaunchKernelGGL((dequantize_lpb<FF, true>), grid, block, 0, st, codes, scales, aux, nb, y);
-    else hipLaunchKernelGGL((dequantize_lpb<FF, false>), grid, block, 0, st, codes, scales, aux, nb, y);
+  if (fmt == F_AXS6) {
+    if (bf16) hipLaunchKernelGGL(dequantize_axs6<true>, grid, block, 0, st, codes, scales, aux, nb, y);
+    else hipLaunchKernelGGL(dequantize_axs6<false>, grid, block, 0, st, codes, scales, aux, nb, y);
+    return hipGetLastError();
+  }
+  MXK_SWITCH_MX(fmt, {
+    if (bf16) hipLaunchKernelGGL((dequantize_mx<FF, true>), grid, block, 0, st, codes, scales, nb, y);
+    else hipLaunchKernelGGL((dequantize_mx<FF, false>), grid, block, 0, st, codes, scales, nb, y);
   });
   return hipGetLastError();
 }
@@ -339,9 +453,14 @@ hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_
 hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,
                                 hipStream_t st) {
   const dim3 grid = grid_for(nb, 256), block(256);
-  MXK_SWITCH_FMT(fmt, {
-    if (bf16) hipLaunchKernelGGL((fake_quantize_lpb<FF, true>), grid, block, 0, st, x, nb, y);
-    else hipLaunchKernelGGL((fake_quantize_lpb<FF, false>), grid, block, 0, st, x, nb, y);
+  if (fmt == F_AXS6) {
+    if (bf16) hipLaunchKernelGGL(fake_quantize_axs6<true>, grid, block, 0, st, x, nb, y);
+    else hipLaunchKernelGGL(fake_quantize_axs6<false>, grid, block, 0, st, x, nb, y);
+    return hipGetLastError();
+  }
+  MXK_SWITCH_MX(fmt, {
+    if (bf16) hipLaunchKernelGGL((fake_quantize_mx<FF, true>), grid, block, 0, st, x, nb, y);
+    else hipLaunchKernelGGL((fake_quantize_mx<FF, false>), grid, block, 0, st, x, nb, y);
   });
   return hipGetLastError();
 }
@@ -349,13 +468,9 @@ hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, v
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
                                    void* codes, uint8_t* scales, hipStream_t st) {
   const dim3 grid = grid_for(rows, 4), block(256);
-  switch (fmt) {
-    case F_E2M3: hipLaunchKernelGGL((softmax_quantize_rows<F_E2M3>), grid, block, 0, st, s, rows, cols, codes, scales); break;
-    case F_E3M2: hipLaunchKernelGGL((softmax_quantize_rows<F_E3M2>), grid, block, 0, st, s, rows, cols, codes, scales); break;
-    case F_E2M1: hipLaunchKernelGGL((softmax_quantize_rows<F_E2M1>), grid, block, 0, st, s, rows, cols, codes, scales); break;
-    case F_E4M3: hipLaunchKernelGGL((softmax_quantize_rows<F_E4M3>), grid, block, 0, st, s, rows, cols, codes, scales); break;
-    default: return hipErrorInvalidValue;
-  }
+  MXK_SWITCH_MX(fmt, {
+    hipLaunchKernelGGL((softmax_quantize_rows<FF>), grid, block, 0, st, s, rows, cols, codes, scales);
+  });
   return hipGetLastError();
 }
 
