@@ -38,11 +38,18 @@ CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
 
 
 def source_digest() -> str:
+    """Digest of the kernel sources with comments and whitespace removed, so
+    that counter figures stay attached to the code they were taken on."""
+    import re
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
+            h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

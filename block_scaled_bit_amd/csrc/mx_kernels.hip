@@ -11,7 +11,7 @@
 //
 // Rules: "Online MXFP6" page ("Start a model": packed codes and an E8M0
 // scale per 32 values); "EFQ-Softmax" explainer (exponent-only block scale
-// from the block's local maximum; exp-then-quantize); "AXS-6" page
+// from the largest magnitude inside the block; exp-then-quantize); "AXS-6" page
 // ("Overview" block layout; "Quick Start" fused fake-quantize).
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -4,20 +4,22 @@
  *
  * The method: every block of 32 contiguous values along the last dimension
  * shares one power-of-two scale chosen from the block's largest magnitude,
- * and each value is stored as a low-bit element code under that scale.
- *   - "Online MXFP6" (Sonar feature page), "Start a model": packed six-bit
- *     data and an E8M0 scale for each block of 32 values; "Select the FP6
- *     encoding": E2M3 (more mantissa) or E3M2 (larger finite range);
- *     "Current limits": dense dimensions are multiples of 128, unsupported
- *     layers stay in BF16.
+ * and every value becomes a low-bit element code relative to that scale.
+ *   - "Online MXFP6" (Sonar feature page), "Start a model": a tensor is
+ *     replaced by six-bit codes, packed, plus one E8M0 scale per 32-value
+ *     block; "Select the FP6 encoding": E2M3 keeps more mantissa, E3M2 more
+ *     range; "Current limits": dense dimensions are required to be 128-
+ *     aligned, and a layer the converter cannot handle is left in BF16 with a
+ *     warning.
  *   - "EFQ-Softmax" explainer, "Jargon" and article: MXFP4 = E2M1 codes
  *     under one block scale; the scale is exponent-only and comes from the
- *     block's local maximum; exp-then-quantize probability generation.
+ *     largest magnitude inside the block; exp-then-quantize probability
+ *     generation.
  *   - "AXS-6: Adaptive eXponent Sharing", "Overview": one 8-bit shared
  *     exponent and a 2-bit config per 32 values, sign + 5-bit mantissa per
- *     value; "Quick Start": fused_fake_quantize(x, block_size=32).
- *   - "eXmY" abstract: non-power-of-two bit widths packed with no wasted
- *     bits while staying byte addressable.
+ *     value; "Quick Start": a fused fake-quantize call on 32-value blocks.
+ *   - "eXmY" abstract: codes whose width is not a power of two are packed
+ *     densely (no padding bits) while blocks stay byte addressable.
  *
  * Rules (identical to the CPU oracle's):
  *   scale byte  0xFF if the block holds a NaN or an infinity; 0 if every

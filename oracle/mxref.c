@@ -30,11 +30,12 @@
 /* [MXFP6] "Start a model" / "Select the FP6 encoding": OCP MXFP6 with  */
 /* E2M3 (more mantissa) or E3M2 (more range), an E8M0 scale per 32.     */
 /* [EFQ] "Jargon": E2M1 = 1 sign, 2 exponent, 1 mantissa bit.           */
-/* [AXS6] "Overview": FP8 E4M3 = [sign:1][exponent:4][mantissa:3].      */
+/* [AXS6] "Overview": FP8 E4M3 has 1 sign, 4 exponent, 3 mantissa bits. */
 /* Biases and ranges follow the OCP MX definitions the [MXFP6] page     */
 /* invokes by name (a reading: the pages print no bias).                */
-/* [AXS6] "Overview": [sign:1][mantissa:5] per value; read as a uniform */
-/* sign-magnitude grid m/16, m = 0..31, under the shared exponent.     */
+/* [AXS6] "Overview": a sign bit and 5 mantissa bits per value; read as  */
+/* a uniform sign-magnitude grid m/16, m = 0..31, under the shared     */
+/* exponent.                                                            */
 /* ------------------------------------------------------------------ */
 typedef struct {
   int bits;          /* code width including the sign bit */
@@ -99,7 +100,8 @@ double mxref_decode(int fmt, int code) {
 /* ------------------------------------------------------------------ */
 /* Q1 + Q2: the shared scale of one block.                             */
 /* [EFQ] article: the block scale is exponent-only and is chosen from  */
-/* the block's local maximum; [EFQ] "Jargon": from that block alone.   */
+/* the largest magnitude inside the block; [EFQ] "Jargon": no other    */
+/* block influences it.                                                 */
 /* [MXFP6] "Start a model": an E8M0 scale per block of 32 values.      */
 /* Reading (OCP conversion rule): byte = floor(log2 amax) - emax + 127,*/
 /* clamped to 0..254; amax == 0 gives byte 0; any NaN or inf in the    */
@@ -161,10 +163,11 @@ int mxref_encode(int fmt, double v, int byte) {
 
 /* ------------------------------------------------------------------ */
 /* Q4: packing of one block's 32 codes.                                */
-/* [EXMY] abstract: non-power-of-two widths packed with no wasted bits */
-/* and byte addressability; [MXFP6] "Start a model": packed six-bit    */
-/* data.  Reading: the codes form a little-endian bit stream, code k   */
-/* at stream bits [k*w, k*w + w), stream bit s in bit s%8 of byte s/8. */
+/* [EXMY] abstract: codes whose width is not a power of two are packed */
+/* densely while staying byte addressable; [MXFP6] "Start a model":    */
+/* six-bit codes, packed.  Reading: the codes form a little-endian bit */
+/* stream, code k at stream bits [k*w, k*w + w), stream bit s in bit   */
+/* s%8 of byte s/8.                                                    */
 /* For 6-bit codes every 4 codes fill 3 bytes; 4-bit codes put the     */
 /* even element in the low nibble; 8-bit codes are one per byte.       */
 /* ------------------------------------------------------------------ */
@@ -308,7 +311,8 @@ int mxref_dequantize(int fmt, int block, const uint8_t *codes,
 /* ------------------------------------------------------------------ */
 /* F: fake-quantize = dequantize(quantize(x)) in the input type, one   */
 /* block at a time with no packed intermediate ([AXS6] "Quick Start":  */
-/* fused_fake_quantize(x, block_size=32), no intermediate allocation). */
+/* a fused fake-quantize call over 32-value blocks that allocates no   */
+/* intermediate buffer).                                                */
 /* ------------------------------------------------------------------ */
 int mxref_fake_quantize(int fmt, int block, int dtype, const void *x, void *y,
                         int64_t rows, int64_t cols) {
