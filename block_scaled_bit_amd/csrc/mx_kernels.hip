@@ -369,15 +369,16 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
 // exact power-of-two products.  Constants: log2(e), ln2 and 1/k! rounded to
 // fp32; head = ln2's fp32 significand cut to 16 bits, tail = fp32(ln2 - head).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_fixed(float d) {
+__device__ __forceinline__ float exp_nonpos(float d) {
+  // d is s - rowmax, so d <= 0 (or -inf); NaN rows never get here.  The
+  // reduction runs on max(d, -104): from there the product below already
+  // rounds to +0, which is the exact result for every d < -104 too.
   const float kLog2e = 0x1.715476p+0f;
   const float kLn2Hi = 0x1.62e400p-1f;
   const float kLn2Lo = 0x1.7f7d1cp-20f;
   const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
               k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
-  // the reduction runs on d clamped into [-104, 88.75] (NaN -> -104) so the
-  // integer n stays in range; the selects below handle the outside
-  const float dc = fminf(fmaxf(d, -104.0f), 88.75f);
+  const float dc = fmaxf(d, -104.0f);
   const float nf = __builtin_rintf(dc * kLog2e);
   float r = __builtin_fmaf(-nf, kLn2Hi, dc);
   r = __builtin_fmaf(-nf, kLn2Lo, r);
@@ -389,16 +390,9 @@ __device__ __forceinline__ float exp_fixed(float d) {
   p = __builtin_fmaf(p, r, k2);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  int n = (int)nf;
-  if (n < -100) { p = p * 0x1p-50f; n += 50; }
-  if (n > 100) { p = p * 0x1p+50f; n -= 50; }
-  float res = p * __uint_as_float((uint32_t)(n + 127) << 23);
-  // outside the reduction's range: below -104 the result rounds to +0,
-  // above 88.75 it overflows; NaN propagates
-  res = (d < -104.0f) ? 0.0f : res;
-  res = (d > 88.75f) ? __builtin_inff() : res;
-  res = (d != d) ? d : res;
-  return res;
+  // p * 2^n with one rounding (n in [-150, 0]; subnormal results rounded to
+  // nearest even), the same value as exact power-of-two pre-scaling
+  return __builtin_ldexpf(p, (int)nf);
 }
 
 __device__ __forceinline__ float wave_max(float m) {
@@ -413,7 +407,35 @@ __device__ __forceinline__ int wave_or(int f) {
   return f;
 }
 
+// Probabilities of one block of shifted scores, quantized; `kind` is the
+// row's case: 0 finite row max, 1 row max +inf (then s - m is -inf, giving
+// P = 0, except NaN where s is +inf itself).
 template <int F>
+__device__ __forceinline__ void probs_block(const uint32_t (&sv)[32], float m, int kind,
+                                           uint32_t (&o)[Fmt<F>::W], uint32_t& byte) {
+  uint32_t v[32];
+  if (kind == 0) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_nonpos(__uint_as_float(sv[k]) - m));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = (sv[k] == 0x7F800000u) ? 0x7FC00000u : 0u;
+  }
+  uint32_t amax = 0u;  // P >= 0 (or NaN), so the bit patterns order as values
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = max(amax, v[k]);
+  byte = scale_byte_from_amax<F>(amax);
+  encode_f32<F>(v, scale_operand(byte), o);
+  if (byte == 0xFFu) {
+#pragma unroll
+    for (int k = 0; k < Fmt<F>::W; ++k) o[k] = 0u;
+  }
+}
+
+// One wavefront per row.  RB > 0: lane l keeps blocks l, l+64, ... (at most
+// RB of them, enough for the whole row) in registers, so the row is read
+// once.  RB == 0: rows of any length; the second pass reads the row again.
+template <int F, int RB>
 __global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __restrict__ s,
                                                              int64_t rows, int64_t cols,
                                                              void* __restrict__ codes,
@@ -425,35 +447,74 @@ __global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __rest
   for (int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); row < rows;
        row += waves) {
     const float* srow = s + row * cols;
-    // pass 1: exact row maximum (a NaN anywhere makes it NaN)
+    uint32_t keep[RB > 0 ? RB : 1][32];
+    // pass 1: exact row maximum; a NaN anywhere poisons the whole row
     float m = -__builtin_inff();
-    int has_nan = 0;
-    for (int64_t j = lane; j < nbr; j += 64) {
-      uint32_t v[32];
-      load_f32_block(srow, j, v);
+    bool nan_seen = false;
+    if constexpr (RB > 0) {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        has_nan |= (v[k] & 0x7FFFFFFFu) > 0x7F800000u;
-        m = fmaxf(m, __uint_as_float(v[k]));
+      for (int i = 0; i < RB; ++i) {
+        const int64_t j = lane + 64 * i;
+        if (j < nbr) {
+          load_f32_block(srow, j, keep[i]);
+#pragma unroll
+          for (int k = 0; k < 32; ++k) {
+            const float x = __uint_as_float(keep[i][k]);
+            nan_seen |= (x != x);
+            m = fmaxf(m, x);
+          }
+        }
+      }
+    } else {
+      for (int64_t j = lane; j < nbr; j += 64) {
+        uint32_t v[32];
+        load_f32_block(srow, j, v);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const float x = __uint_as_float(v[k]);
+          nan_seen |= (x != x);
+          m = fmaxf(m, x);
+        }
       }
     }
     m = wave_max(m);
-    if (wave_or(has_nan)) m = __builtin_nanf("");
-    // pass 2: P = exp(s - m), then quantize each block of P
-    for (int64_t j = lane; j < nbr; j += 64) {
-      uint32_t v[32], o[W];
-      load_f32_block(srow, j, v);
+    // a NaN in the row, or a row of only -inf (then s - m = -inf - -inf is
+    // NaN everywhere), poisons every block of the row
+    const bool row_nan = wave_or(nan_seen ? 1 : 0) != 0 || m == -__builtin_inff();
+    const int kind = (m == __builtin_inff()) ? 1 : 0;
+    // pass 2: P = exp(s - m) per block, then quantize the block
+    if constexpr (RB > 0) {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_fixed(__uint_as_float(v[k]) - m));
-      const uint32_t byte = scale_byte_from_amax<F>(amax_f32x32(v));
-      encode_f32<F>(v, scale_operand(byte), o);
-      if (byte == 0xFFu) {
+      for (int i = 0; i < RB; ++i) {
+        const int64_t j = lane + 64 * i;
+        if (j < nbr) {
+          uint32_t o[W];
+          uint32_t byte = 0xFFu;
+          if (row_nan) {
 #pragma unroll
-        for (int k = 0; k < W; ++k) o[k] = 0u;
+            for (int k = 0; k < W; ++k) o[k] = 0u;
+          } else {
+            probs_block<F>(keep[i], m, kind, o, byte);
+          }
+          store_codes<W>(codes, row * nbr + j, o);
+          scales[row * nbr + j] = (uint8_t)byte;
+        }
       }
-      const int64_t b = row * nbr + j;
-      store_codes<W>(codes, b, o);
-      scales[b] = (uint8_t)byte;
+    } else {
+      for (int64_t j = lane; j < nbr; j += 64) {
+        uint32_t o[W];
+        uint32_t byte = 0xFFu;
+        if (row_nan) {
+#pragma unroll
+          for (int k = 0; k < W; ++k) o[k] = 0u;
+        } else {
+          uint32_t sv[32];
+          load_f32_block(srow, j, sv);
+          probs_block<F>(sv, m, kind, o, byte);
+        }
+        store_codes<W>(codes, row * nbr + j, o);
+        scales[row * nbr + j] = (uint8_t)byte;
+      }
     }
   }
 }
@@ -525,8 +586,17 @@ hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, v
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
                                    void* codes, uint8_t* scales, hipStream_t st) {
   const dim3 grid = grid_for(rows, 4), block(256);
+  const int64_t nbr = cols / 32;
+  // rows of up to 64, 128 or 256 blocks stay in registers (read once)
   MXK_SWITCH_MX(fmt, {
-    hipLaunchKernelGGL((softmax_quantize_rows<FF>), grid, block, 0, st, s, rows, cols, codes, scales);
+    if (nbr <= 64)
+      hipLaunchKernelGGL((softmax_quantize_rows<FF, 1>), grid, block, 0, st, s, rows, cols, codes, scales);
+    else if (nbr <= 128)
+      hipLaunchKernelGGL((softmax_quantize_rows<FF, 2>), grid, block, 0, st, s, rows, cols, codes, scales);
+    else if (nbr <= 256)
+      hipLaunchKernelGGL((softmax_quantize_rows<FF, 4>), grid, block, 0, st, s, rows, cols, codes, scales);
+    else
+      hipLaunchKernelGGL((softmax_quantize_rows<FF, 0>), grid, block, 0, st, s, rows, cols, codes, scales);
   });
   return hipGetLastError();
 }

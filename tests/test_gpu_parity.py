@@ -144,8 +144,11 @@ def test_fake_quantize_parity_and_in_place(mx, fmt, dtype):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3], ids=lambda f: FMT_NAMES[f])
-def test_softmax_quantize_parity(mx, fmt):
-    s = workloads.attn_scores(rows=37, cols=4096 + 96)
+@pytest.mark.parametrize("cols", [1024, 4096, 4096 + 96, 8192 + 32])
+def test_softmax_quantize_parity(mx, fmt, cols):
+    # the column counts cover rows held in registers (up to 64, 128 and 256
+    # blocks per row) and rows streamed twice (longer)
+    s = workloads.attn_scores(rows=37, cols=cols)
     s[3, 11] = np.nan
     s[4, 5] = np.inf
     s[5, :] = -np.inf
