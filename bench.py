@@ -101,7 +101,15 @@ def headline(mx, x_np, steps, warmup):
             raise mx.MxError(st, "mx_quantize")
 
     ms = time_launches(step, nsets, steps, warmup)
-    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0]
+
+    # the same HBM, same rotation: a plain device-to-device copy of the input
+    # (reads and writes in_bytes each) as a measured streaming ceiling
+    def copy(i):
+        xs[(i + 1) % nsets].copy_(xs[i])
+
+    ms_copy = time_launches(copy, nsets, max(50, steps // 10), 20)
+    copy_gbs = 2 * in_bytes / ms_copy / 1e6
+    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs
 
 
 def secondary(mx, steps):
@@ -270,7 +278,7 @@ def main():
         return
 
     x = workloads.linear_weight()
-    ms, in_b, alg_b, nsets, codes0, scales0 = headline(mx, x, args.steps, args.warmup)
+    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs = headline(mx, x, args.steps, args.warmup)
     achieved = alg_b / ms / 1e6
     digest = source_digest()
     out = {
@@ -294,6 +302,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(digest)},
+        "copy_ceiling": {"d2d_copy_GBps": round(copy_gbs, 1),
+                         "frac_of_copy": round(achieved / copy_gbs, 4),
+                         "note": "device-to-device copy of the bf16 input (read + write "
+                                 "bytes / time), same buffers and rotation"},
     }
     if not args.no_cpu_baseline:
         base, parity, nrows = cpu_baseline(x, codes0, scales0)

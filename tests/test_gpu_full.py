@@ -140,3 +140,30 @@ def test_activations_dynamic_round_trip(mx, fmt):
     # 41943 blocks were zeroed; a few of them later received an inf or a NaN
     assert np.all(gs[zero] == 0) and 41943 - 13422 <= zero.sum() <= 41943 + 100
     assert torch.equal(y.view(torch.int16), fq.view(torch.int16))
+
+
+def test_offsets_beyond_4gib(mx):
+    """A 4.3 GB bf16 tensor: block and byte offsets pass 2^32, so 64-bit
+    address arithmetic in every kernel matters.  The columns repeat a
+    4096-wide seeded tile, so the expected blocks are the oracle's blocks of
+    that tile."""
+    tile = workloads.linear_weight(rows=9, cols=4096)
+    reps = 1 << 16                                   # 9 rows of 2^28 values: 4.8 GB
+    rows, cols = 9, 4096 * reps
+    xd = to_dev(tile).repeat(1, reps)
+    assert xd.numel() * 2 > (1 << 32)
+    codes, scales, _ = mx.quantize(xd, "mxfp6_e2m3")
+    y = mx.dequantize(codes, scales, None, "mxfp6_e2m3", torch.bfloat16)
+    torch.cuda.synchronize()
+    oc, os_, _ = oracle.quantize(0, tile)
+    want_y = oracle.dequantize(0, oc, os_, None, 9, 4096, oracle.BF16)
+    nbr = cols // 32
+    for j0 in (0, nbr // 2, nbr - 128):             # first, middle and last 128-block span
+        gc = to_host(codes[:, j0:j0 + 128])
+        gs = to_host(scales[:, j0:j0 + 128])
+        assert_bytes_equal(gs, os_, f"scales at block {j0}")
+        assert_bytes_equal(gc, oc, f"codes at block {j0}", 24)
+        gy = to_host(y[:, j0 * 32:(j0 + 128) * 32])
+        assert_bytes_equal(gy, want_y, f"dequantized at block {j0}")
+    del xd, codes, scales, y
+    torch.cuda.empty_cache()
