@@ -217,3 +217,37 @@ def test_device_argument_errors(mx):
     assert mx.mx_quantize(0, 64, 0, x, 4, 64, codes, scales, None) == 4
     assert mx.mx_softmax_quantize(4, 32, x, 4, 64, codes, scales) == 4
     assert mx.mx_quantize(0, 32, 0, x, 0, 64, codes, scales, None) == 0
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: FMT_NAMES[f])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("nblocks", [1, 63, 64, 65, 1000])
+def test_wide_outputs_stay_in_bounds(mx, fmt, dtype, nblocks):
+    # dequantize and fake-quantize write whole 64-block tiles through LDS;
+    # a ragged last tile must write exactly its own bytes and nothing after
+    rng = np.random.default_rng(50 + nblocks)
+    rows, cols = nblocks, 32
+    x = _special_input(rng, rows, cols, dtype)
+    elt = 2 if dtype == "bf16" else 4
+    guard = 4096
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ybuf = torch.full((guard + rows * cols + guard,), float("nan"), dtype=tdt, device="cuda")
+    ybuf.view(torch.int16 if dtype == "bf16" else torch.int32).fill_(0x5A5A)
+    sentinel = to_host(ybuf[:guard]).copy()
+    xd = to_dev(x)
+    assert mx.mx_fake_quantize(fmt, 32, mx.MX_BF16 if dtype == "bf16" else mx.MX_FP32, xd,
+                               ybuf[guard:guard + rows * cols], rows, cols) == 0
+    torch.cuda.synchronize()
+    yh = to_host(ybuf)
+    assert np.array_equal(yh[:guard], sentinel) and np.array_equal(yh[guard + rows * cols:], sentinel)
+    assert_bytes_equal(yh[guard:guard + rows * cols], oracle.fake_quantize(fmt, x).reshape(-1), "fq")
+    oc, os_, oa = oracle.quantize(fmt, x)
+    ybuf.view(torch.int16 if dtype == "bf16" else torch.int32).fill_(0x5A5A)
+    assert mx.mx_dequantize(fmt, 32, to_dev(oc), to_dev(os_), to_dev(oa) if fmt == 4 else None,
+                            rows, cols, mx.MX_BF16 if dtype == "bf16" else mx.MX_FP32,
+                            ybuf[guard:guard + rows * cols]) == 0
+    torch.cuda.synchronize()
+    yh = to_host(ybuf)
+    assert np.array_equal(yh[:guard], sentinel) and np.array_equal(yh[guard + rows * cols:], sentinel)
+    want = oracle.dequantize(fmt, oc, os_, oa, rows, cols, oracle.BF16 if dtype == "bf16" else oracle.FP32)
+    assert_bytes_equal(yh[guard:guard + rows * cols], want.reshape(-1), "dq", 32 * elt)
