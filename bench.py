@@ -187,6 +187,38 @@ def secondary(mx, steps):
     record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
     del sd, c, sc
 
+    # layer-by-layer conversion of a synthetic dense decoder (4 layers,
+    # hidden 4096, MLP 14336, 1024-wide k/v): weights already on the GPU, and
+    # again from pinned host memory (that rate includes the PCIe upload)
+    from block_scaled_bit_amd import convert
+    g = torch.Generator(device="cuda").manual_seed(11)
+    shapes = {"self_attn.q_proj": (4096, 4096), "self_attn.k_proj": (1024, 4096),
+              "self_attn.v_proj": (1024, 4096), "self_attn.o_proj": (4096, 4096),
+              "mlp.gate_proj": (14336, 4096), "mlp.up_proj": (14336, 4096),
+              "mlp.down_proj": (4096, 14336)}
+    model = {f"model.layers.{i}.{k}.weight": (torch.randn(v, generator=g, device="cuda") * 0.02)
+             .to(torch.bfloat16) for i in range(4) for k, v in shapes.items()}
+    cfg = convert.QuantConfig.from_options("mxfp6")
+    in_b = sum(t.numel() * 2 for t in model.values())
+    out_b = sum(t.numel() // 32 * 25 for t in model.values())
+    for src_name, src in (("device", model), ("pinned_host", None)):
+        if src is None:
+            src = {k: v.cpu().pin_memory() for k, v in model.items()}
+        convert.convert_model(src, cfg)  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 5
+        for _ in range(reps):
+            out, _ = convert.convert_model(src, cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        record(f"convert_dense_4_layers_from_{src_name}", ms, in_b, out_b,
+               "synthetic decoder, 4 layers x 7 weights, hidden 4096, MLP 14336 (mxfp6 shorthand)")
+        del out
+    del model, src
+
     # small fp32 tensor: latency of the three ops
     xsm = torch.from_numpy(workloads.weights_small()).cuda()
     cc = torch.empty(1024 * 24, dtype=torch.uint8, device="cuda")

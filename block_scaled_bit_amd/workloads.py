@@ -92,6 +92,46 @@ def activations(rows=16384, cols=8192, seed=None) -> np.ndarray:
     return to_bf16_bits(x)
 
 
+def synthetic_model(layers=2, hidden=256, intermediate=512, kv=128, vocab=1000, experts=4,
+                    moe_intermediate=128, moe_layers=(1,), seed=7) -> dict:
+    """Tensor names and shapes of a small decoder (attention projections,
+    dense or mixture-of-experts MLPs with a router gate, a shared expert and
+    its gate, norms, embeddings, output head), every weight N(0, 0.02^2) in
+    bf16 bits.  Stands in for a checkpoint being loaded."""
+    rng = np.random.default_rng(seed)
+
+    def w(*shape):
+        return to_bf16_bits((0.02 * rng.standard_normal(shape)).astype(np.float32))
+
+    t = {"model.embed_tokens.weight": w(vocab, hidden)}
+    for i in range(layers):
+        p = f"model.layers.{i}."
+        t[p + "input_layernorm.weight"] = to_bf16_bits(np.ones(hidden, np.float32))
+        t[p + "self_attn.q_proj.weight"] = w(hidden, hidden)
+        t[p + "self_attn.k_proj.weight"] = w(kv, hidden)
+        t[p + "self_attn.v_proj.weight"] = w(kv, hidden)
+        t[p + "self_attn.o_proj.weight"] = w(hidden, hidden)
+        t[p + "post_attention_layernorm.weight"] = to_bf16_bits(np.ones(hidden, np.float32))
+        if i in moe_layers:
+            t[p + "mlp.gate.weight"] = w(experts, hidden)
+            for e in range(experts):
+                q = p + f"mlp.experts.{e}."
+                t[q + "gate_proj.weight"] = w(moe_intermediate, hidden)
+                t[q + "up_proj.weight"] = w(moe_intermediate, hidden)
+                t[q + "down_proj.weight"] = w(hidden, moe_intermediate)
+            for nm in ("gate_proj", "up_proj"):
+                t[p + f"mlp.shared_expert.{nm}.weight"] = w(moe_intermediate, hidden)
+            t[p + "mlp.shared_expert.down_proj.weight"] = w(hidden, moe_intermediate)
+            t[p + "mlp.shared_expert_gate.weight"] = w(1, hidden)
+        else:
+            t[p + "mlp.gate_proj.weight"] = w(intermediate, hidden)
+            t[p + "mlp.up_proj.weight"] = w(intermediate, hidden)
+            t[p + "mlp.down_proj.weight"] = w(hidden, intermediate)
+    t["model.norm.weight"] = to_bf16_bits(np.ones(hidden, np.float32))
+    t["lm_head.weight"] = w(vocab, hidden)
+    return t
+
+
 GENERATORS = {
     "weights_small": weights_small,
     "axs6_weight": axs6_weight,
