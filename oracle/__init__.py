@@ -21,10 +21,37 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 FP6_E2M3, FP6_E3M2, FP4_E2M1, FP8_E4M3, AXS6 = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
 BLOCK = 32
-BYTES_PER_BLOCK = {FP6_E2M3: 24, FP6_E3M2: 24, FP4_E2M1: 16, FP8_E4M3: 32, AXS6: 24}
-CODE_BITS = {FP6_E2M3: 6, FP6_E3M2: 6, FP4_E2M1: 4, FP8_E4M3: 8, AXS6: 6}
 NAMES = {"mxfp6_e2m3": FP6_E2M3, "mxfp6_e3m2": FP6_E3M2, "mxfp4": FP4_E2M1,
          "mxfp8": FP8_E4M3, "axs6": AXS6}
+
+
+def exmy(e: int, m: int) -> int:
+    """Identifier of the generic eXmY format with e exponent and m mantissa
+    bits (width 1 + e + m, 3..9 bits, e <= 7)."""
+    return 0x100 | (e << 4) | m
+
+
+EXMY_FORMATS = [exmy(e, w - 1 - e) for w in range(3, 10) for e in range(0, min(w - 1, 7) + 1)
+                if w - 1 - e >= 0]
+
+
+class _Table(dict):
+    """Per-format constant that also answers for generic eXmY identifiers."""
+
+    def __init__(self, base, generic):
+        super().__init__(base)
+        self._generic = generic
+
+    def __missing__(self, fmt):
+        if (fmt & ~0xFF) == 0x100:
+            return self._generic((fmt >> 4) & 0xF, fmt & 0xF)
+        raise KeyError(fmt)
+
+
+CODE_BITS = _Table({FP6_E2M3: 6, FP6_E3M2: 6, FP4_E2M1: 4, FP8_E4M3: 8, AXS6: 6},
+                   lambda e, m: 1 + e + m)
+BYTES_PER_BLOCK = _Table({FP6_E2M3: 24, FP6_E3M2: 24, FP4_E2M1: 16, FP8_E4M3: 32, AXS6: 24},
+                         lambda e, m: 4 * (1 + e + m))
 
 
 def _load():

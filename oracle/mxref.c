@@ -59,13 +59,50 @@ static const fmt_t FORMATS[5] = {
 
 #define BLOCK 32
 
-static const fmt_t *get_fmt(int fmt) {
-  return (fmt >= 0 && fmt <= 4) ? &FORMATS[fmt] : 0;
+/* ------------------------------------------------------------------ */
+/* Generic eXmY formats ([EXMY] abstract: every split of a bit width   */
+/* into exponent and mantissa bits, e.g. e0m6 .. e6m0 for 7 bits).      */
+/* Identifier 0x100 | e << 4 | m; width w = 1 + e + m, 3 <= w <= 9,     */
+/* e <= 7.  Reading: sign-magnitude, IEEE-style fields with bias        */
+/* 2^(e-1) - 1 and subnormals, every code finite (no inf/NaN codes, as  */
+/* in the OCP FP6/FP4 formats); e = 0 is a plain integer magnitude m.   */
+/* ------------------------------------------------------------------ */
+static int make_exmy(int e, int m, fmt_t *f) {
+  int w = 1 + e + m;
+  if (e < 0 || m < 0 || e > 7 || w < 3 || w > 9) return 0;
+  f->bits = w;
+  f->ebits = e;
+  f->mbits = m;
+  f->nan_mag = -1;
+  f->fixed_point = 0;
+  f->bpb = 4 * w;
+  if (e >= 1) {
+    f->bias = (1 << (e - 1)) - 1;
+    f->emin = 1 - f->bias;
+    f->emax = ((1 << e) - 1) - f->bias;                 /* top field is finite */
+    f->maxnorm = ldexp(2.0 - ldexp(1.0, -m), f->emax);
+  } else {
+    f->bias = 0;
+    f->emin = m;                  /* every magnitude is "subnormal": step 1 */
+    f->emax = m - 1;
+    f->maxnorm = ldexp(1.0, m) - 1.0;
+  }
+  return 1;
+}
+
+/* Fills *f for a format identifier; 0 if the identifier is unsupported. */
+static int get_fmt(int fmt, fmt_t *f) {
+  if (fmt >= 0 && fmt <= 4) {
+    *f = FORMATS[fmt];
+    return 1;
+  }
+  if ((fmt & ~0xFF) == 0x100) return make_exmy((fmt >> 4) & 0xF, fmt & 0xF, f);
+  return 0;
 }
 
 int mxref_bytes_per_block(int fmt) {
-  const fmt_t *f = get_fmt(fmt);
-  return f ? f->bpb : -1;
+  fmt_t f;
+  return get_fmt(fmt, &f) ? f.bpb : -1;
 }
 
 /* floor(log2(a)) for a finite a > 0, exactly */
@@ -79,7 +116,8 @@ static int ilog2(double a) {
 /* Decoding one code (sign included) to its unscaled value.            */
 /* ------------------------------------------------------------------ */
 double mxref_decode(int fmt, int code) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int sign = (code >> (f->bits - 1)) & 1;
   int mag = code & ((1 << (f->bits - 1)) - 1);
   double v;
@@ -110,7 +148,8 @@ double mxref_decode(int fmt, int code) {
 /* 8-bit shared exponent per 32 values).                                */
 /* ------------------------------------------------------------------ */
 int mxref_scale_byte(int fmt, const double *v, int n) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   double amax = 0.0;
   int i, b;
   for (i = 0; i < n; i++) /* Q1: classify */
@@ -128,12 +167,25 @@ int mxref_scale_byte(int fmt, const double *v, int n) {
 /* Q3: one element.                                                    */
 /* a = |v| / 2^(byte-127) (exact); a is clamped to the largest finite  */
 /* magnitude (saturation, never NaN from a finite input); the code is  */
-/* the grid point nearest to a, ties to the code whose last bit is 0   */
-/* (round-to-nearest-even); the sign bit is copied, so -0 and negative */
-/* values that round to zero keep it.                                  */
+/* the grid point nearest to a, and on an exact tie the code whose     */
+/* last bit is 0 (round-to-nearest-even on the codes); the sign bit is */
+/* copied, so -0 and negative values that round to zero keep it.       */
 /* ------------------------------------------------------------------ */
+
+/* magnitude code of a grid value r (r >= 0 on the grid of f) */
+static int code_of_value(const fmt_t *f, double r) {
+  if (r < ldexp(1.0, f->emin)) /* subnormal code (every code when e = 0) */
+    return (int)(r / ldexp(1.0, f->emin - f->mbits));
+  {
+    int er = ilog2(r);
+    int mant = (int)((r / ldexp(1.0, er) - 1.0) * (double)(1 << f->mbits));
+    return ((er + f->bias) << f->mbits) | mant;
+  }
+}
+
 int mxref_encode(int fmt, double v, int byte) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   double X = ldexp(1.0, byte - 127);
   double a = fabs(v) / X;
   int sign = signbit(v) ? 1 : 0;
@@ -148,15 +200,12 @@ int mxref_encode(int fmt, double v, int byte) {
     int ea = ilog2(a);
     int eu = ea > f->emin ? ea : f->emin;       /* binade of the step */
     double u = ldexp(1.0, eu - f->mbits);       /* grid step at a */
-    double n = nearbyint(a / u);                /* RNE (default mode) */
-    double r = n * u;                           /* the chosen grid value */
-    if (r < ldexp(1.0, f->emin)) {              /* subnormal code */
-      mag = (int)(r / ldexp(1.0, f->emin - f->mbits));
-    } else {                                    /* normal code */
-      int er = ilog2(r);
-      int mant = (int)((r / ldexp(1.0, er) - 1.0) * (double)(1 << f->mbits));
-      mag = ((er + f->bias) << f->mbits) | mant;
-    }
+    double nlo = floor(a / u);                  /* a / u is exact */
+    double rlo = nlo * u, rhi = (nlo + 1.0) * u; /* neighbouring grid values */
+    int clo = code_of_value(f, rlo), chi = code_of_value(f, rhi);
+    if (a - rlo < rhi - a) mag = clo;
+    else if (a - rlo > rhi - a) mag = chi;
+    else mag = (clo % 2 == 0) ? clo : chi;      /* tie: the even code */
   }
   return (sign << (f->bits - 1)) | mag;
 }
@@ -246,7 +295,8 @@ static void store_value(int dtype, void *y, int64_t i, double v) {
 }
 
 static int check_args(int fmt, int block, int64_t rows, int64_t cols) {
-  if (!get_fmt(fmt) || block != BLOCK) return -1;
+  fmt_t f;
+  if (!get_fmt(fmt, &f) || block != BLOCK) return -1;
   if (rows < 0 || cols < 0 || cols % BLOCK) return -1;
   return 0;
 }
@@ -263,7 +313,8 @@ static int quantize_values(const fmt_t *f, int fmt, const double *v, int *c) {
 int mxref_quantize(int fmt, int block, int in_dtype, const void *x,
                    int64_t rows, int64_t cols, uint8_t *codes,
                    uint8_t *scales, uint8_t *aux) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int64_t nb, b;
   double v[BLOCK];
   int c[BLOCK], k;
@@ -289,7 +340,8 @@ int mxref_quantize(int fmt, int block, int in_dtype, const void *x,
 int mxref_dequantize(int fmt, int block, const uint8_t *codes,
                      const uint8_t *scales, const uint8_t *aux, int64_t rows,
                      int64_t cols, int out_dtype, void *y) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int64_t nb, b;
   int c[BLOCK], k;
   if (check_args(fmt, block, rows, cols)) return -1;
@@ -316,7 +368,8 @@ int mxref_dequantize(int fmt, int block, const uint8_t *codes,
 /* ------------------------------------------------------------------ */
 int mxref_fake_quantize(int fmt, int block, int dtype, const void *x, void *y,
                         int64_t rows, int64_t cols) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int64_t nb, b;
   double v[BLOCK];
   int c[BLOCK], k, byte;
@@ -405,7 +458,8 @@ int mxref_softmax_probs(const float *s, int64_t rows, int64_t cols, float *p) {
 
 int mxref_softmax_quantize(int fmt, int block, const float *s, int64_t rows,
                            int64_t cols, uint8_t *codes, uint8_t *scales) {
-  const fmt_t *f = get_fmt(fmt);
+  fmt_t fs;
+  const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int64_t r, j, nbr;
   double v[BLOCK];
   int c[BLOCK], k;

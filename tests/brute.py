@@ -23,8 +23,48 @@ import numpy as np
 import torch
 
 E2M3, E3M2, E2M1, E4M3, AXS6 = 0, 1, 2, 3, 4
-CODE_BITS = {E2M3: 6, E3M2: 6, E2M1: 4, E4M3: 8, AXS6: 6}
-BPB = {E2M3: 24, E3M2: 24, E2M1: 16, E4M3: 32, AXS6: 24}
+
+
+def is_exmy(fmt):
+    return (fmt & ~0xFF) == 0x100
+
+
+def exmy_em(fmt):
+    return (fmt >> 4) & 0xF, fmt & 0xF
+
+
+class _Table(dict):
+    def __init__(self, base, generic):
+        super().__init__(base)
+        self._generic = generic
+
+    def __missing__(self, fmt):
+        if is_exmy(fmt):
+            return self._generic(*exmy_em(fmt))
+        raise KeyError(fmt)
+
+
+CODE_BITS = _Table({E2M3: 6, E3M2: 6, E2M1: 4, E4M3: 8, AXS6: 6}, lambda e, m: 1 + e + m)
+BPB = _Table({E2M3: 24, E3M2: 24, E2M1: 16, E4M3: 32, AXS6: 24}, lambda e, m: 4 * (1 + e + m))
+
+
+def exmy_grid(e: int, m: int) -> np.ndarray:
+    """Magnitudes of a generic eXmY format by enumeration of its fields:
+    e = 0: the integers 0 .. 2^m - 1; e >= 1: field f = 0 gives mant/2^m *
+    2^(1 - bias), f >= 1 gives (1 + mant/2^m) * 2^(f - bias), bias =
+    2^(e-1) - 1, every field finite.  (Pinned against library dtypes and
+    closed forms in tests/test_oracle_exmy.py.)"""
+    if e == 0:
+        return np.arange(2 ** m, dtype=np.float64)
+    bias = 2 ** (e - 1) - 1
+    vals = []
+    for f in range(2 ** e):
+        for mant in range(2 ** m):
+            if f == 0:
+                vals.append(math.ldexp(mant / 2 ** m, 1 - bias))
+            else:
+                vals.append(math.ldexp(1 + mant / 2 ** m, f - bias))
+    return np.array(vals, dtype=np.float64)
 
 
 def _torch_decode(dtype) -> np.ndarray:
@@ -33,6 +73,8 @@ def _torch_decode(dtype) -> np.ndarray:
 
 def grid(fmt: int) -> np.ndarray:
     """Magnitudes indexed by magnitude code (NaN where the code is NaN)."""
+    if is_exmy(fmt):
+        return exmy_grid(*exmy_em(fmt))
     if fmt == E4M3:
         return _torch_decode(torch.float8_e4m3fn)[:128].copy()
     if fmt == E2M3:
