@@ -140,7 +140,14 @@ def secondary(mx, steps):
             record("quantize_e3m2", ms, rows * cols * 2, nb * 25, "linear_weight bf16 14336x4096")
         ms = time_launches(lambda i: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
         record(f"dequantize_{nm}_to_bf16", ms, nb * 25, rows * cols * 2, "linear_weight bf16 14336x4096")
-    del xs, cs, ss
+    # a generic eXmY format (7-bit e3m3, 28 B per block; rounding in fp32)
+    g = mx.MX_EXMY(3, 3)
+    cg = [torch.empty(nb * 28, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ms = time_launches(lambda i: mx.mx_quantize(g, 32, 0, xs[i], rows, cols, cg[i], ss[i], None, stream), n, k, 3)
+    record("quantize_exmy_e3m3", ms, rows * cols * 2, nb * 29, "linear_weight bf16 14336x4096")
+    ms = time_launches(lambda i: mx.mx_dequantize(g, 32, cg[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+    record("dequantize_exmy_e3m3_to_bf16", ms, nb * 29, rows * cols * 2, "linear_weight bf16 14336x4096")
+    del xs, cs, ss, cg
 
     # AXS-6 weight: fake-quantize and quantize
     a = workloads.axs6_weight()

@@ -16,7 +16,7 @@ import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
 
 __all__ = [
     "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
-    "FORMATS", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
+    "FORMATS", "MX_EXMY", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
     "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "quantize", "dequantize",
     "fake_quantize", "softmax_quantize", "library_path",
 ]
@@ -24,8 +24,23 @@ __all__ = [
 MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3, MX_AXS6 = 0, 1, 2, 3, 4
 MX_BF16, MX_FP32 = 0, 1
 BLOCK = 32
-BYTES_PER_BLOCK = {0: 24, 1: 24, 2: 16, 3: 32, 4: 24}
-# format names used by the pages' configuration strings
+
+
+def MX_EXMY(e: int, m: int) -> int:
+    """Generic eXmY format id (width 1 + e + m in 3..9, e <= 7), as mx.h."""
+    return 0x100 | (e << 4) | m
+
+
+class _BytesPerBlock(dict):
+    def __missing__(self, fmt):
+        if (fmt & ~0xFF) == 0x100:
+            return 4 * (1 + ((fmt >> 4) & 0xF) + (fmt & 0xF))
+        raise KeyError(fmt)
+
+
+BYTES_PER_BLOCK = _BytesPerBlock({0: 24, 1: 24, 2: 16, 3: 32, 4: 24})
+# format names used by the pages' configuration strings; "eXmY" strings
+# (e.g. "e3m3") name the generic formats
 FORMATS = {"mxfp6": MX_FP6_E2M3, "mxfp6_e2m3": MX_FP6_E2M3, "mxfp6_e3m2": MX_FP6_E3M2,
            "mxfp4": MX_FP4_E2M1, "mxfp8": MX_FP8_E4M3, "axs6": MX_AXS6}
 
@@ -64,7 +79,15 @@ _lib = _load()
 
 
 def _fmt(f) -> int:
-    return FORMATS[f] if isinstance(f, str) else int(f)
+    if isinstance(f, str):
+        if f in FORMATS:
+            return FORMATS[f]
+        import re
+        m = re.fullmatch(r"e(\d)m(\d)", f)
+        if m:
+            return MX_EXMY(int(m.group(1)), int(m.group(2)))
+        raise KeyError(f"unknown format name {f!r}")
+    return int(f)
 
 
 def _ptr(t) -> int | None:

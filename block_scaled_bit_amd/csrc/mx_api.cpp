@@ -1,6 +1,7 @@
 // mx_api.cpp -- the C ABI declared in include/mx.h: host-side validation and
 // dispatch to the gfx950 kernels.  Nothing here allocates or keeps state.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "mx.h"
@@ -10,7 +11,37 @@ namespace {
 
 constexpr int kBytesPerBlock[5] = {24, 24, 16, 32, 24};
 
-bool fmt_ok(int f) { return f >= MX_FP6_E2M3 && f <= MX_AXS6; }
+bool is_exmy(int f) { return (f & ~0xFF) == 0x100; }
+int exmy_e(int f) { return (f >> 4) & 0xF; }
+int exmy_m(int f) { return f & 0xF; }
+int exmy_width(int f) { return 1 + exmy_e(f) + exmy_m(f); }
+
+bool fmt_ok(int f) {
+  if (f >= MX_FP6_E2M3 && f <= MX_AXS6) return true;
+  return is_exmy(f) && exmy_e(f) <= 7 && exmy_width(f) >= 3 && exmy_width(f) <= 9;
+}
+
+int bytes_per_block(int f) { return is_exmy(f) ? 4 * exmy_width(f) : kBytesPerBlock[f]; }
+
+// The generic format's parameters: sign-magnitude, bias 2^(e-1) - 1 with
+// subnormals and no special codes; e = 0 is an integer magnitude.
+mxk::ExmyParams exmy_params(int f) {
+  const int e = exmy_e(f), m = exmy_m(f);
+  mxk::ExmyParams p;
+  p.m = m;
+  if (e >= 1) {
+    const int bias = (1 << (e - 1)) - 1;
+    p.emin = 1 - bias;
+    p.emax = ((1 << e) - 1) - bias;
+    p.maxf = ldexpf(2.0f - ldexpf(1.0f, -m), p.emax);
+  } else {
+    p.emin = m;
+    p.emax = m - 1;
+    p.maxf = ldexpf(1.0f, m) - 1.0f;
+  }
+  p.bias = 1 - p.emin;
+  return p;
+}
 bool dtype_ok(int d) { return d == MX_BF16 || d == MX_FP32; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,7 +83,7 @@ mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
   mx_status st = check_common(fmt, block, rows, cols, &nothing);
   if (st != MX_OK) return st;
   const int64_t nb = nothing ? 0 : rows * (cols / MX_BLOCK);
-  if (code_bytes) *code_bytes = (size_t)nb * (size_t)kBytesPerBlock[fmt];
+  if (code_bytes) *code_bytes = (size_t)nb * (size_t)bytes_per_block(fmt);
   if (scale_bytes) *scale_bytes = (size_t)nb;
   if (aux_bytes) *aux_bytes = (fmt == MX_AXS6) ? (size_t)((nb + 3) / 4) : 0u;
   return MX_OK;
@@ -68,6 +99,9 @@ mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype, const void* x
   if (!x || !codes || !scales || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
   const int64_t nb = rows * (cols / MX_BLOCK);
+  if (is_exmy(fmt))
+    return from_hip(mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype == MX_BF16, x,
+                                     nullptr, nb, codes, scales, static_cast<hipStream_t>(stream)));
   return from_hip(mxk::launch_quantize(fmt, in_dtype == MX_BF16, x, nb, codes, scales, aux,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -83,6 +117,9 @@ mx_status mx_dequantize(mx_format fmt, int block, const void* codes, const uint8
   if (!codes || !scales || !y || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
   if (!aligned16(codes) || !aligned16(y)) return MX_ERR_ALIGN;
   const int64_t nb = rows * (cols / MX_BLOCK);
+  if (is_exmy(fmt))
+    return from_hip(mxk::launch_exmy(1, exmy_width(fmt), exmy_params(fmt), out_dtype == MX_BF16,
+                                     codes, scales, nb, y, nullptr, static_cast<hipStream_t>(stream)));
   return from_hip(mxk::launch_dequantize(fmt, out_dtype == MX_BF16, codes, scales, aux, nb, y,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -97,6 +134,9 @@ mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype, const void*
   if (!x || !y) return MX_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
   const int64_t nb = rows * (cols / MX_BLOCK);
+  if (is_exmy(fmt))
+    return from_hip(mxk::launch_exmy(2, exmy_width(fmt), exmy_params(fmt), dtype == MX_BF16, x,
+                                     nullptr, nb, y, nullptr, static_cast<hipStream_t>(stream)));
   return from_hip(mxk::launch_fake_quantize(fmt, dtype == MX_BF16, x, nb, y,
                                             static_cast<hipStream_t>(stream)));
 }
@@ -106,7 +146,7 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float* s, int64_t 
   bool nothing = false;
   mx_status st = check_common(fmt, block, rows, cols, &nothing);
   if (st != MX_OK) return st;
-  if (fmt == MX_AXS6) return MX_ERR_UNSUPPORTED;
+  if (fmt == MX_AXS6 || is_exmy(fmt)) return MX_ERR_UNSUPPORTED;
   if (nothing) return MX_OK;
   if (!s || !codes || !scales) return MX_ERR_NULL;
   if (!aligned16(s) || !aligned16(codes)) return MX_ERR_ALIGN;

@@ -9,12 +9,29 @@
 
 namespace mxk {
 
+// Generic eXmY format parameters (prepared on the host): m mantissa bits;
+// emin = exponent of the smallest normal (m for integer formats); emax =
+// floor(log2 of the largest magnitude); bias = 1 - emin; maxf = the largest
+// magnitude.
+struct ExmyParams {
+  int m;
+  int emin;
+  int emax;
+  int bias;
+  float maxf;
+};
+
 hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
                            uint8_t* scales, uint8_t* aux, hipStream_t st);
 hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
                              const uint8_t* aux, int64_t nb, void* y, hipStream_t st);
 hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,
                                 hipStream_t st);
+// op 0: quantize (in = x, out = codes, scales_out); op 1: dequantize (in =
+// codes, scales_in, out = y); op 2: fake-quantize (in = x, out = y).
+hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const void* in,
+                       const uint8_t* scales_in, int64_t nb, void* out, uint8_t* scales_out,
+                       hipStream_t st);
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
                                    void* codes, uint8_t* scales, hipStream_t st);
 

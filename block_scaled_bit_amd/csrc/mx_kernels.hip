@@ -361,6 +361,153 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Generic eXmY formats (the eXmY abstract: any split of a bit width into
+// exponent and mantissa bits): no hardware conversion exists for most of
+// them, so rounding is done in fp32.  W (3..9 bits) is a template parameter;
+// the split comes in ExmyParams.
+// Rounding of a scaled, clamped magnitude a (exact in fp32): the grid step
+// at a is 2^(max(floor(log2 a), emin) - m).  Adding C = 2^(that exponent +
+// 23) makes the fp32 adder's round-to-nearest-even land on that step (the
+// sum lies in [C, 2C), whose ulp is the step), so n = bits(a + C) - bits(C)
+// counts steps and mag = n + (binade - emin) << m.  Ties then go to the
+// even n, which is the even code whenever m >= 1; with m = 0 (exponent only)
+// a tie 1.5 * 2^k would pick the larger value, so an odd code there is
+// moved down by one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t exmy_round(float a, const ExmyParams& p) {
+  const uint32_t ab = __float_as_uint(a);
+  const int ea = (int)(ab >> 23);
+  const int et = ea > 127 + p.emin ? ea : 127 + p.emin;
+  const float C = __uint_as_float((uint32_t)(et + 23 - p.m) << 23);
+  const float sum = a + C;
+  uint32_t mag = (__float_as_uint(sum) - __float_as_uint(C)) + ((uint32_t)(et - 127 - p.emin) << p.m);
+  if (p.m == 0 && ea >= 127 + p.emin && (ab & 0x7FFFFFu) == 0x400000u && (mag & 1u)) mag -= 1u;
+  return mag;
+}
+
+__device__ __forceinline__ float exmy_decode(uint32_t mag, int scale_exp, const ExmyParams& p) {
+  const uint32_t e = mag >> p.m;
+  const uint32_t mant = mag & ((1u << p.m) - 1u);
+  const uint32_t sig = e ? (mant | (1u << p.m)) : mant;
+  const int ex = (int)(e ? e : 1u) - p.bias - p.m;  // bias = 1 - emin
+  return __builtin_ldexpf((float)sig, ex + scale_exp);
+}
+
+__device__ __forceinline__ uint32_t exmy_block_byte(const uint32_t (&v)[32], const ExmyParams& p) {
+  uint32_t amax = 0u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = max(amax, v[k] & 0x7FFFFFFFu);
+  if (amax >= 0x7F800000u) return 0xFFu;
+  if (amax == 0u) return 0u;
+  const int field = (int)(amax >> 23);
+  const int e = field ? field - 127 : (31 - __builtin_clz(amax)) - 149;
+  int b = e - p.emax + 127;
+  b = b < 0 ? 0 : b;
+  return (uint32_t)(b > 254 ? 254 : b);
+}
+
+template <int W>
+__device__ __forceinline__ void exmy_codes(const uint32_t (&v)[32], uint32_t byte,
+                                           const ExmyParams& p, uint32_t (&c)[32]) {
+  const int neg_exp = 127 - (int)byte;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const float a = fminf(__builtin_ldexpf(__uint_as_float(v[k] & 0x7FFFFFFFu), neg_exp), p.maxf);
+    c[k] = (byte == 0xFFu) ? 0u : (exmy_round(a, p) | ((v[k] >> 31) << (W - 1)));
+  }
+}
+
+template <int W, bool BF16>
+__global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x, int64_t nb,
+                                                     uint32_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales, ExmyParams p) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    uint32_t v[32], c[32], o[W];
+    load_values<BF16>(x, b, v);
+    const uint32_t byte = exmy_block_byte(v, p);
+    exmy_codes<W>(v, byte, p, c);
+    pack32<W>(c, o);
+#pragma unroll
+    for (int j = 0; j < W; ++j) codes[b * W + j] = o[j];  // 4W bytes per block
+    scales[b] = (uint8_t)byte;
+  }
+}
+
+template <int W, bool BF16>
+__global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t nb, void* y,
+                                                          ExmyParams p) {
+  constexpr int NCH = BF16 ? 4 : 8;
+  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
+    const int64_t b0 = t * kTile, b = b0 + lane;
+    uint32_t v[32] = {}, c[32], out[32];
+    if (b < nb) load_values<BF16>(x, b, v);
+    const uint32_t byte = exmy_block_byte(v, p);
+    exmy_codes<W>(v, byte, p, c);
+    const int sexp = (int)byte - 127;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float val = exmy_decode(c[k] & ((1u << (W - 1)) - 1u), sexp, p);  // exact
+      out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(val) | (v[k] & 0x80000000u));
+    }
+    if constexpr (BF16) {
+      // the results are bf16 values: round to nearest even (exact unless a
+      // subnormal product needs it)
+      uint32_t d[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        d[k] = f32_to_bf16_rne(__uint_as_float(out[2 * k])) |
+               (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
+      store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
+    } else {
+      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+    }
+  }
+}
+
+template <int W, bool BF16>
+__global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       int64_t nb, void* __restrict__ y,
+                                                       ExmyParams p) {
+  constexpr int NCH = BF16 ? 4 : 8;
+  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
+    const int64_t b0 = t * kTile, b = b0 + lane;
+    uint32_t o[W] = {};
+    uint32_t byte = 0;
+    if (b < nb) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) o[j] = codes[b * W + j];
+      byte = scales[b];
+    }
+    const int sexp = (int)byte - 127;
+    uint32_t out[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t code = unpack1<W>(o, k);
+      const float val = exmy_decode(code & ((1u << (W - 1)) - 1u), sexp, p);
+      out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(val) | ((code >> (W - 1)) << 31));
+    }
+    if constexpr (BF16) {
+      uint32_t d[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        d[k] = f32_to_bf16_rne(__uint_as_float(out[2 * k])) |
+               (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
+      store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
+    } else {
+      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Exp-then-quantize probabilities: one wavefront per row.
 // exp_fixed is the fp32 op sequence of the library's contract: Cody-Waite
 // reduction (Cody and Waite, "Software Manual for the Elementary
@@ -597,6 +744,38 @@ hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_
       hipLaunchKernelGGL((softmax_quantize_rows<FF, 4>), grid, block, 0, st, s, rows, cols, codes, scales);
     else
       hipLaunchKernelGGL((softmax_quantize_rows<FF, 0>), grid, block, 0, st, s, rows, cols, codes, scales);
+  });
+  return hipGetLastError();
+}
+
+#define MXK_SWITCH_WIDTH(w, BODY)                           \
+  switch (w) {                                              \
+    case 3: { constexpr int WW = 3; BODY; } break;          \
+    case 4: { constexpr int WW = 4; BODY; } break;          \
+    case 5: { constexpr int WW = 5; BODY; } break;          \
+    case 6: { constexpr int WW = 6; BODY; } break;          \
+    case 7: { constexpr int WW = 7; BODY; } break;          \
+    case 8: { constexpr int WW = 8; BODY; } break;          \
+    case 9: { constexpr int WW = 9; BODY; } break;          \
+    default: return hipErrorInvalidValue;                   \
+  }
+
+hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const void* in,
+                       const uint8_t* scales_in, int64_t nb, void* out, uint8_t* scales_out,
+                       hipStream_t st) {
+  const dim3 block(256);
+  const dim3 grid = (op == 0) ? grid_for(nb, 256) : grid_for(nb, 4 * kTile);
+  MXK_SWITCH_WIDTH(width, {
+    if (op == 0) {
+      if (bf16) hipLaunchKernelGGL((quantize_exmy<WW, true>), grid, block, 0, st, in, nb, (uint32_t*)out, scales_out, p);
+      else hipLaunchKernelGGL((quantize_exmy<WW, false>), grid, block, 0, st, in, nb, (uint32_t*)out, scales_out, p);
+    } else if (op == 1) {
+      if (bf16) hipLaunchKernelGGL((dequantize_exmy<WW, true>), grid, block, 0, st, (const uint32_t*)in, scales_in, nb, out, p);
+      else hipLaunchKernelGGL((dequantize_exmy<WW, false>), grid, block, 0, st, (const uint32_t*)in, scales_in, nb, out, p);
+    } else {
+      if (bf16) hipLaunchKernelGGL((fake_quantize_exmy<WW, true>), grid, block, 0, st, in, nb, out, p);
+      else hipLaunchKernelGGL((fake_quantize_exmy<WW, false>), grid, block, 0, st, in, nb, out, p);
+    }
   });
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@
  * cols / 32 blocks, block b = row * (cols/32) + j):
  *   x, y     [rows, cols] bf16 or fp32, 16-byte aligned
  *   codes    [rows, cols/32, bpb] bytes, bpb = 24 (FP6, AXS-6), 16 (FP4),
- *            32 (FP8); 16-byte aligned
+ *            32 (FP8), 4w (eXmY of width w); 16-byte aligned
  *   scales   [rows, cols/32] bytes (E8M0; AXS-6 shared exponent, same
  *            encoding)
  *   aux      AXS-6 only: ceil(nb/4) bytes, block b's 2-bit config in bits
@@ -76,6 +76,18 @@ typedef enum {
   MX_FP8_E4M3 = 3, /* OCP MXFP8 E4M3 ("mxfp8") */
   MX_AXS6 = 4      /* AXS-6: shared exponent, sign + 5-bit mantissa */
 } mx_format;
+
+/* Generic eXmY formats ("eXmY" abstract: every split of a bit width into
+ * exponent and mantissa bits): identifier 0x100 | e << 4 | m, width
+ * w = 1 + e + m between 3 and 9 bits, e <= 7.  Sign-magnitude codes with
+ * IEEE-style fields (bias 2^(e-1) - 1, subnormals) and no special codes;
+ * e = 0 is an integer magnitude 0 .. 2^m - 1.  Scale byte as above with
+ * emax = floor(log2 of the largest magnitude); ties go to the even code
+ * (for m = 0 that is the even exponent field).  Codes pack like the other
+ * formats: 32 codes of w bits = 4w bytes per block.  AXS-6 equals e0m5
+ * with its scale byte 4 higher (where neither byte is clamped).  Not
+ * accepted by mx_softmax_quantize. */
+#define MX_EXMY(e, m) ((mx_format)(0x100 | ((e) << 4) | (m)))
 
 typedef enum { MX_BF16 = 0, MX_FP32 = 1 } mx_dtype;
 
