@@ -76,8 +76,10 @@ def _load():
     lib.mxref_exp.restype = ctypes.c_float
     lib.mxref_softmax_probs.argtypes = [P, I64, I64, P]
     lib.mxref_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P]
+    lib.mxref_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I,
+                                        I, P, P, P, P, P]
     for f in ("mxref_quantize", "mxref_dequantize", "mxref_fake_quantize",
-              "mxref_softmax_probs", "mxref_softmax_quantize"):
+              "mxref_softmax_probs", "mxref_softmax_quantize", "mxref_attention_fwd"):
         getattr(lib, f).restype = I
     return lib
 
@@ -196,3 +198,35 @@ def softmax_quantize(fmt: int, s: np.ndarray):
         raise ValueError("oracle softmax_quantize: bad arguments")
     nbr = cols // BLOCK
     return codes.reshape(rows, nbr, BYTES_PER_BLOCK[fmt]), scales.reshape(rows, nbr)
+
+
+def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,
+                  v_scales: np.ndarray, scale: float, kv_tile: int = 64, out_dtype: int = FP32):
+    """Attention forward with E2M1 probabilities (online softmax over
+    `kv_tile` keys at a time).  q [heads, lq, d] and k [heads, lk, d] are
+    bf16 bit patterns; v_codes/v_scales are V^T ([heads, d, lk]) quantized
+    with ``quantize(v_fmt, .)``.  Returns (o [heads, lq, d], row_max,
+    row_sum [heads, lq], p_codes [heads, lq, lk/32, 16], p_scales
+    [heads, lq, lk/32])."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    heads, lq, d = q.shape
+    lk = k.shape[1]
+    if k.shape != (heads, lk, d):
+        raise ValueError("q and k must be [heads, lq, d] and [heads, lk, d]")
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    v_scales = np.ascontiguousarray(v_scales, dtype=np.uint8)
+    nbk = lk // BLOCK
+    if v_codes.size != heads * d * nbk * BYTES_PER_BLOCK[v_fmt] or v_scales.size != heads * d * nbk:
+        raise ValueError("v_codes / v_scales do not match V^T [heads, d, lk]")
+    o = np.empty((heads, lq, d), np.uint16 if out_dtype == BF16 else np.float32)
+    row_max = np.empty((heads, lq), np.float32)
+    row_sum = np.empty((heads, lq), np.float32)
+    p_codes = np.empty((heads, lq, nbk, 16), np.uint8)
+    p_scales = np.empty((heads, lq, nbk), np.uint8)
+    rc = _lib.mxref_attention_fwd(v_fmt, BLOCK, _ptr(q), _ptr(k), _ptr(v_codes), _ptr(v_scales),
+                                  heads, lq, lk, d, float(scale), kv_tile, out_dtype, _ptr(o),
+                                  _ptr(row_max), _ptr(row_sum), _ptr(p_codes), _ptr(p_scales))
+    if rc:
+        raise ValueError("oracle attention_fwd: bad arguments")
+    return o, row_max, row_sum, p_codes, p_scales

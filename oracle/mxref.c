@@ -23,6 +23,7 @@
 #include "mxref.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------ */
@@ -487,5 +488,133 @@ int mxref_softmax_quantize(int fmt, int block, const float *s, int64_t rows,
       pack_block(f, c, codes + b * f->bpb);
     }
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention forward with exp-then-quantize probabilities.             */
+/* [EFQ] "Does it change FlashAttention?" and the stage table: the     */
+/* online softmax keeps a running row maximum, rescales the earlier    */
+/* partial sums when it grows, accumulates in high precision and       */
+/* normalizes once at the end; the probabilities are produced by exp() */
+/* of the shifted scores and quantized to block-scaled E2M1 (MXFP4)     */
+/* before the PV product; [EFQ] stage table, "Denominator operand":    */
+/* the E2M1 block also feeds the denominator (the conventional path    */
+/* leaves this open; reading: the same operand, as in the EFQ path).   */
+/* Readings where the pages are silent:                                */
+/*  - scores s = q . k from bf16 q, k, summed in double and rounded     */
+/*    once to fp32; t = fp32(s * scale);                               */
+/*  - the running maximum is updated once per kv_tile keys (NaN scores */
+/*    are skipped by the maximum, as fmax does); alpha =               */
+/*    exp_ref(m_old - m_new) rescales the sums only when m grows;      */
+/*  - p = exp_ref(fp32(t - m_new)), quantized per 32 keys to E2M1 by   */
+/*    the MX rules above (a NaN p poisons its block, so the row's       */
+/*    output is NaN);                                                   */
+/*  - V arrives transposed and block-quantized along the keys (V^T as  */
+/*    [d, lk] in any MX element format), and is decoded exactly;        */
+/*  - l and the numerator are accumulated in double from the decoded   */
+/*    E2M1 values; o = numerator / l, rounded once to the output type. */
+/* Layouts: q [heads, lq, d], k [heads, lk, d] (bf16 bits); v_codes    */
+/* [heads, d, lk/32, bpb], v_scales [heads, d, lk/32]; o [heads, lq,   */
+/* d]; row_max, row_sum [heads, lq] (the final m and fp32(l));         */
+/* p_codes [heads, lq, lk/32, 16], p_scales [heads, lq, lk/32]: the    */
+/* E2M1 blocks as they entered the PV product.  The last four may be   */
+/* NULL.                                                                */
+/* ------------------------------------------------------------------ */
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float fv;
+  memcpy(&fv, &u, 4);
+  return (double)fv;
+}
+
+int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
+                        const uint16_t *k, const uint8_t *v_codes,
+                        const uint8_t *v_scales, int64_t heads, int64_t lq,
+                        int64_t lk, int64_t d, float scale, int kv_tile,
+                        int out_dtype, void *o, float *row_max,
+                        float *row_sum, uint8_t *p_codes, uint8_t *p_scales) {
+  fmt_t fv, fp;
+  int64_t h, i, j, c, kk, nbk;
+  double *vhat = 0, *acc = 0;
+  float *t = 0;
+  if (!get_fmt(v_fmt, &fv) || v_fmt == MXREF_AXS6 || (v_fmt & ~0xFF)) return -1;
+  get_fmt(MXREF_FP4_E2M1, &fp);
+  if (block != BLOCK || heads < 0 || lq < 0 || d <= 0 || lk <= 0 ||
+      lk % BLOCK || kv_tile <= 0 || kv_tile % BLOCK)
+    return -1;
+  nbk = lk / BLOCK;
+  vhat = (double *)malloc(sizeof(double) * (size_t)(d * lk));
+  acc = (double *)malloc(sizeof(double) * (size_t)d);
+  t = (float *)malloc(sizeof(float) * (size_t)lk);
+  if (!vhat || !acc || !t) {
+    free(vhat); free(acc); free(t);
+    return -1;
+  }
+  for (h = 0; h < heads; h++) {
+    /* decode V^T of this head: vhat[c * lk + key] */
+    for (c = 0; c < d; c++)
+      for (j = 0; j < nbk; j++) {
+        int64_t b = (h * d + c) * nbk + j;
+        int codes[BLOCK], e;
+        int byte = v_scales[b];
+        unpack_block(&fv, v_codes + b * fv.bpb, codes);
+        for (e = 0; e < BLOCK; e++)
+          vhat[c * lk + j * BLOCK + e] =
+              byte == 0xFF ? NAN
+                           : mxref_decode(v_fmt, codes[e]) * ldexp(1.0, byte - 127);
+      }
+    for (i = 0; i < lq; i++) {
+      const uint16_t *qi = q + (h * lq + i) * d;
+      float m = -INFINITY;
+      double l = 0.0;
+      int64_t row = h * lq + i;
+      /* scores of the whole row, t = fp32(fp32(q . k) * scale) */
+      for (kk = 0; kk < lk; kk++) {
+        const uint16_t *kr = k + (h * lk + kk) * d;
+        double s = 0.0;
+        for (c = 0; c < d; c++) s += bf16_value(qi[c]) * bf16_value(kr[c]);
+        t[kk] = (float)s * scale;
+      }
+      for (c = 0; c < d; c++) acc[c] = 0.0;
+      for (j = 0; j < lk; j += kv_tile) {
+        int64_t end = j + kv_tile < lk ? j + kv_tile : lk;
+        float m_new = m;
+        for (kk = j; kk < end; kk++)
+          if (t[kk] > m_new) m_new = t[kk]; /* NaN never compares greater */
+        if (m_new > m) {
+          double alpha = (double)mxref_exp(m - m_new);
+          l *= alpha;
+          for (c = 0; c < d; c++) acc[c] *= alpha;
+          m = m_new;
+        }
+        for (kk = j; kk < end; kk += BLOCK) {
+          double pv[BLOCK], phat[BLOCK];
+          int codes[BLOCK], e, byte;
+          for (e = 0; e < BLOCK; e++) {
+            float dd = t[kk + e] - m;
+            pv[e] = (double)mxref_exp(dd);
+          }
+          byte = quantize_values(&fp, MXREF_FP4_E2M1, pv, codes);
+          for (e = 0; e < BLOCK; e++)
+            phat[e] = byte == 0xFF ? NAN
+                                   : mxref_decode(MXREF_FP4_E2M1, codes[e]) *
+                                         ldexp(1.0, byte - 127);
+          if (p_codes) pack_block(&fp, codes, p_codes + (row * nbk + kk / BLOCK) * fp.bpb);
+          if (p_scales) p_scales[row * nbk + kk / BLOCK] = (uint8_t)byte;
+          for (e = 0; e < BLOCK; e++) {
+            l += phat[e];
+            for (c = 0; c < d; c++) acc[c] += phat[e] * vhat[c * lk + kk + e];
+          }
+        }
+      }
+      for (c = 0; c < d; c++) store_value(out_dtype, o, row * d + c, acc[c] / l);
+      if (row_max) row_max[row] = m;
+      if (row_sum) row_sum[row] = (float)l;
+    }
+  }
+  free(vhat);
+  free(acc);
+  free(t);
   return 0;
 }

@@ -61,6 +61,16 @@ int   mxref_softmax_quantize(int fmt, int block, const float *s,
                              int64_t rows, int64_t cols,
                              uint8_t *codes, uint8_t *scales);
 
+/* attention forward: online softmax over kv_tile keys at a time, exp
+ * then E2M1 quantization of the probabilities, V^T block-quantized along
+ * the keys (layouts next to the definition in mxref.c) */
+int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
+                        const uint16_t *k, const uint8_t *v_codes,
+                        const uint8_t *v_scales, int64_t heads, int64_t lq,
+                        int64_t lk, int64_t d, float scale, int kv_tile,
+                        int out_dtype, void *o, float *row_max,
+                        float *row_sum, uint8_t *p_codes, uint8_t *p_scales);
+
 #ifdef __cplusplus
 }
 #endif
