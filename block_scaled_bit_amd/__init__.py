@@ -17,8 +17,9 @@ import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
 __all__ = [
     "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
     "FORMATS", "MX_EXMY", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
-    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "quantize", "dequantize",
-    "fake_quantize", "softmax_quantize", "library_path",
+    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd", "quantize",
+    "dequantize", "fake_quantize", "softmax_quantize", "quantize_v", "attention_fwd",
+    "library_path",
 ]
 
 MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3, MX_AXS6 = 0, 1, 2, 3, 4
@@ -69,8 +70,10 @@ def _load():
     lib.mx_dequantize.argtypes = [I, I, P, P, P, I64, I64, I, P, P]
     lib.mx_fake_quantize.argtypes = [I, I, I, P, P, I64, I64, P]
     lib.mx_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P, P]
+    lib.mx_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I, P,
+                                     P, P, P, P, P]
     for f in ("mx_buffer_sizes", "mx_quantize", "mx_dequantize", "mx_fake_quantize",
-              "mx_softmax_quantize"):
+              "mx_softmax_quantize", "mx_attention_fwd"):
         getattr(lib, f).restype = I
     return lib
 
@@ -150,6 +153,14 @@ def mx_softmax_quantize(fmt, block, s, rows, cols, codes, scales, stream=None) -
                                     _ptr(scales), _stream(stream))
 
 
+def mx_attention_fwd(v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d, scale, out_dtype,
+                     o, row_max, row_sum, p_codes, p_scales, stream=None) -> int:
+    return _lib.mx_attention_fwd(_fmt(v_fmt), block, _ptr(q), _ptr(k), _ptr(v_codes),
+                                 _ptr(v_scales), heads, lq, lk, d, float(scale), out_dtype, _ptr(o),
+                                 _ptr(row_max), _ptr(row_sum), _ptr(p_codes), _ptr(p_scales),
+                                 _stream(stream))
+
+
 # ---------------------------------------------------------------------------
 # tensor-level helpers (allocate outputs with torch)
 # ---------------------------------------------------------------------------
@@ -222,3 +233,50 @@ def softmax_quantize(s: torch.Tensor, fmt="mxfp4", block: int = BLOCK):
     scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=s.device)
     _check(mx_softmax_quantize(f, block, s, rows, cols, codes, scales), "mx_softmax_quantize")
     return codes, scales
+
+
+def quantize_v(v: torch.Tensor, fmt="mxfp8"):
+    """V [heads, lk, d] -> (codes, scales) of V^T [heads, d, lk] in blocks of
+    32 keys, the layout attention_fwd reads.  The transpose is a torch copy
+    (memory plumbing); the quantization runs in the library."""
+    if v.dim() != 3:
+        raise ValueError("v must be [heads, lk, d]")
+    codes, scales, _ = quantize(v.transpose(1, 2).contiguous(), fmt)
+    return codes, scales
+
+
+def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
+                  v_scales: torch.Tensor, v_fmt="mxfp8", scale=None, out_dtype=torch.bfloat16,
+                  stats: bool = False, probs: bool = False):
+    """Attention forward with E2M1 probabilities.  q [heads, lq, 128] and k
+    [heads, lk, 128] bf16; V given as ``quantize_v`` returns it.  Returns o
+    [heads, lq, 128]; with stats=True also (row_max, row_sum); with
+    probs=True also the E2M1 probability blocks (p_codes, p_scales)."""
+    f = _fmt(v_fmt)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise MxError(4, "attention_fwd needs bf16 q and k")
+    for t in (q, k, v_codes, v_scales):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous GPU tensors")
+    heads, lq, d = q.shape
+    lk = k.shape[1]
+    if k.shape != (heads, lk, d):
+        raise ValueError("k must be [heads, lk, d] with q's heads and d")
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty((heads, lq, d), dtype=out_dtype, device=q.device)
+    rm = rs = pc = ps = None
+    if stats:
+        rm = torch.empty((heads, lq), dtype=torch.float32, device=q.device)
+        rs = torch.empty((heads, lq), dtype=torch.float32, device=q.device)
+    if probs:
+        pc = torch.empty((heads, lq, lk // BLOCK, 16), dtype=torch.uint8, device=q.device)
+        ps = torch.empty((heads, lq, lk // BLOCK), dtype=torch.uint8, device=q.device)
+    _check(mx_attention_fwd(f, BLOCK, q, k, v_codes, v_scales, heads, lq, lk, d, scale,
+                            _dtype_code(o), o, rm, rs, pc, ps), "mx_attention_fwd")
+    out = (o,)
+    if stats:
+        out += (rm, rs)
+    if probs:
+        out += (pc, ps)
+    return out[0] if len(out) == 1 else out

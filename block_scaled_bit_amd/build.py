@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mx_api.cpp", "mx_kernels.hip"]
+SOURCES = ["mx_api.cpp", "mx_kernels.hip", "mx_attention.hip"]
 
 # Device flags: gfx950 only; no floating-point contraction (every fused
 # multiply-add in the kernels is written out); no packed-fp32 instruction

@@ -154,4 +154,31 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float* s, int64_t 
                                                static_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_attention_fwd(mx_format v_fmt, int block, const void* q, const void* k,
+                           const void* v_codes, const uint8_t* v_scales, int64_t heads,
+                           int64_t lq, int64_t lk, int64_t d, float scale, mx_dtype out_dtype,
+                           void* o, float* row_max, float* row_sum, void* p_codes,
+                           uint8_t* p_scales, void* stream) {
+  if (!(v_fmt == MX_FP8_E4M3 || v_fmt == MX_FP6_E2M3 || v_fmt == MX_FP6_E3M2 ||
+        v_fmt == MX_FP4_E2M1))
+    return MX_ERR_UNSUPPORTED;
+  if (block != MX_BLOCK || d != 128 || !dtype_ok(out_dtype)) return MX_ERR_UNSUPPORTED;
+  if (heads < 0 || lq < 0 || lk <= 0 || lk % MX_BLOCK != 0) return MX_ERR_SHAPE;
+  // int32 indices inside the kernel: every per-head and grid count must fit
+  if (heads > INT32_MAX || lq > INT32_MAX - 128 || lk > INT32_MAX) return MX_ERR_SHAPE;
+  if (heads * ((lq + 127) / 128) > INT32_MAX) return MX_ERR_SHAPE;
+  if (heads > 0 && lq > 0 && (heads * lq > INT64_MAX / (2 * 128 * 16) ||
+                              heads * lk > INT64_MAX / (2 * 128 * 16)))
+    return MX_ERR_SHAPE;
+  if ((p_codes == nullptr) != (p_scales == nullptr)) return MX_ERR_NULL;
+  if (heads == 0 || lq == 0) return MX_OK;
+  if (!q || !k || !v_codes || !v_scales || !o) return MX_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v_codes) || !aligned16(o) ||
+      (p_codes && !aligned16(p_codes)))
+    return MX_ERR_ALIGN;
+  return from_hip(mxk::launch_attention(v_fmt, out_dtype == MX_BF16, q, k, v_codes, v_scales,
+                                        (int)heads, (int)lq, (int)lk, scale, o, row_max, row_sum,
+                                        p_codes, p_scales, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,334 @@
+// mx_attention.hip -- attention forward with exp-then-quantize E2M1
+// probabilities on gfx950 (device code and its launcher).
+//
+// Method: "EFQ-Softmax: exp-free E2M1 probabilities" (explainer), sections
+// "Does it change FlashAttention?" and the stage table: the online softmax
+// keeps a running row maximum, rescales the earlier sums when it grows,
+// accumulates in high precision and normalizes once; the probabilities are
+// exp() of the shifted scores, quantized to block-scaled E2M1 (MXFP4) for
+// the PV product, and the same E2M1 block feeds the denominator.
+//
+// Work split: one workgroup of 4 waves per (head, 128 queries); each wave
+// owns 32 queries and walks the keys in tiles of 64:
+//   S^T  = K_tile * Q^T      8+8 bf16 32x32x16 MFMAs (two 32-key halves)
+//   swap                     v_permlane32_swap gives each lane the 32 scores
+//                            of one (query, 32-key block) pair
+//   t    = S * scale; tile max; rescale O and l when the maximum grows
+//   p    = exp_ref(t - m); block scale byte; 16 E2M1 codes per lane, which
+//          are exactly the lane's B operand of the block-scaled MFMA
+//   O^T += V^T * P^T         4 block-scaled 32x32x64 MFMAs (V in E4M3,
+//                            E2M3, E3M2 or E2M1, P in E2M1)
+//   l   += 1 * P^T           one more block-scaled MFMA with an all-ones A
+// so the probabilities never leave registers and both the numerator and the
+// denominator consume the same E2M1 operand.  K and V^T tiles are staged in
+// LDS once per workgroup and shared by its 4 waves.
+//
+// Operand layouts (checked on the hardware by the library's probe tests):
+//   bf16 32x32x16: lane l holds A[l%32][8(l/32) + e] and B[8(l/32) + e][l%32]
+//   scaled 32x32x64, FP6/FP4: lane l holds the 32-value block k = 32(l/32)..
+//     of row (A) or column (B) l%32; FP8: bytes 0..15 hold k = 16(l/32) + e
+//     and bytes 16..31 hold k = 32 + 16(l/32) + e; the lane's scale operand
+//     is the E8M0 of block k = 32(l/32).. of that row or column
+//   result: D[8(r/4) + 4(l/32) + r%4][l%32] in accumulator r.
+// The head-dimension index inside the QK^T contraction is permuted (lane
+// half h, step i, element e -> d = 64h + 8i + e) so that every lane reads
+// 128 contiguous bytes of its Q and K rows; the sum is the same.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mx_exp.h"
+#include "mx_formats.h"
+#include "mx_hw.h"
+#include "mx_kernels.h"
+
+namespace mxk {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;              // head dimension
+constexpr int kTile = 64;            // keys per online-softmax step
+constexpr int kWaves = 4;
+constexpr int kRows = 32 * kWaves;   // queries per workgroup
+constexpr int kKPitch = 2 * kD + 16; // bytes per K row in LDS (16 B of padding
+                                     // keep the 16-B row reads conflict-free)
+
+// V operand: instruction format code (0 E4M3, 2 E2M3, 3 E3M2, 4 E2M1) ->
+// packed bytes per 32 values and the LDS row pitch (two blocks + padding)
+template <int VF>
+constexpr int v_bpb() { return VF == 0 ? 32 : (VF == 4 ? 16 : 24); }
+template <int VF>
+constexpr int v_pitch() { return 2 * v_bpb<VF>() + 16; }
+
+// The A operand (V^T row d, lane half h) of the block-scaled MFMA from the
+// LDS copy of the tile's two blocks of that row.
+template <int VF>
+__device__ __forceinline__ i32x8_t load_v_operand(const uint8_t* row, int h) {
+  i32x8_t a = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (VF == 0) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(row + 16 * h);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(row + 32 + 16 * h);
+    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+  } else if constexpr (VF == 4) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + 16 * h);
+    a[0] = w[0]; a[1] = w[1]; a[2] = w[2]; a[3] = w[3];
+  } else {
+    const u32x2_t w0 = *reinterpret_cast<const u32x2_t*>(row + 24 * h);
+    const u32x2_t w1 = *reinterpret_cast<const u32x2_t*>(row + 24 * h + 8);
+    const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(row + 24 * h + 16);
+    a[0] = w0[0]; a[1] = w0[1]; a[2] = w1[0]; a[3] = w1[1]; a[4] = w2[0]; a[5] = w2[1];
+  }
+  return a;
+}
+
+template <int VF, bool OUT_BF16>
+__global__ __launch_bounds__(256) void attention_fwd_mx(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int lq, int lk,
+    float scale, int qtiles, void* __restrict__ o, float* __restrict__ row_max,
+    float* __restrict__ row_sum, uint8_t* __restrict__ pc, uint8_t* __restrict__ ps) {
+  constexpr int BPB = v_bpb<VF>();
+  constexpr int VP = v_pitch<VF>();
+  constexpr int IPD = 2 * BPB / 8;  // 8-byte items per V^T row of a tile
+  __shared__ __align__(16) uint8_t ks[kTile * kKPitch];
+  __shared__ __align__(16) uint8_t vsh[kD * VP];
+  __shared__ uint8_t vsc[kD * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, h = lane >> 5;
+
+  // Workgroup order: the hardware deals consecutive workgroups round-robin
+  // to the 8 XCDs, so renumber them to give each XCD a contiguous range of
+  // (head, query tile) pairs; a head's K and V then stay in one L2.
+  int wg = blockIdx.x;
+  const int total = gridDim.x;
+  if ((total & 7) == 0) wg = (wg & 7) * (total >> 3) + (wg >> 3);
+  const int bh = wg / qtiles, qt = wg - bh * qtiles;
+  const int qrow = qt * kRows + wave * 32 + col;
+  const bool qvalid = qrow < lq;
+  const int nbk = lk / 32;
+  const int ntiles = (lk + kTile - 1) / kTile;
+
+  // Q^T operand: lane holds d = 64h + 8i + e of its query, i = 0..7
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qp = q + ((int64_t)bh * lq + (qvalid ? qrow : 0)) * kD + 64 * h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (qvalid) w = *reinterpret_cast<const u32x4_t*>(qp + 8 * i);
+      qf[i] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  f32x16_t acc[4];  // O^T tile T: d = 32T + 8(r/4) + 4h + r%4, query col
+  f32x16_t lacc;    // every accumulator holds the query's l
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc[0][r] = 0.0f; acc[1][r] = 0.0f; acc[2][r] = 0.0f; acc[3][r] = 0.0f;
+    lacc[r] = 0.0f;
+  }
+  float m = -INFINITY;
+  const i32x8_t ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * kTile;
+    const int kb0 = key0 / 32;
+    const bool two = kb0 + 1 < nbk;  // false only for a last tile of 32 keys
+    __syncthreads();
+    // K tile: 64 rows of 256 B in 16-B chunks (rows past lk read as zero)
+    for (int c = tid; c < kTile * 16; c += 256) {
+      const int r = c >> 4, cc = c & 15;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (key0 + r < lk)
+        w = *reinterpret_cast<const u32x4_t*>(k + ((int64_t)bh * lk + key0 + r) * kD + 8 * cc);
+      *reinterpret_cast<u32x4_t*>(ks + r * kKPitch + 16 * cc) = w;
+    }
+    // V^T tile: 128 rows (d) of two blocks, 8-B items; a missing second
+    // block reads as zero codes under scale 1
+    for (int c = tid; c < kD * IPD; c += 256) {
+      const int dd = c / IPD, it = c - dd * IPD;
+      u32x2_t w = {0u, 0u};
+      if (two || it < IPD / 2)
+        w = *reinterpret_cast<const u32x2_t*>(vc + (((int64_t)bh * kD + dd) * nbk + kb0) * BPB +
+                                              8 * it);
+      *reinterpret_cast<u32x2_t*>(vsh + dd * VP + 8 * it) = w;
+    }
+    if (tid < kD) {
+      const uint8_t* sp = vs + ((int64_t)bh * kD + tid) * nbk + kb0;
+      vsc[2 * tid] = sp[0];
+      vsc[2 * tid + 1] = two ? sp[1] : (uint8_t)127;
+    }
+    __syncthreads();
+
+    // S^T for keys key0 .. +31 (s0) and key0+32 .. +63 (s1)
+    f32x16_t s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(ks + col * kKPitch + 128 * h + 16 * i);
+      const u32x4_t a1 =
+          *reinterpret_cast<const u32x4_t*>(ks + (32 + col) * kKPitch + 128 * h + 16 * i);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), qf[i], s0, 0,
+                                                   0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qf[i], s1, 0,
+                                                   0, 0);
+    }
+    // After the swap every lane holds block h of the tile for its query:
+    // x[r] is key 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4.
+    float x[16], y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0[r]),
+                                                       __float_as_uint(s1[r]), false, false);
+      x[r] = __uint_as_float(sw[0]) * scale;
+      y[r] = __uint_as_float(sw[1]) * scale;
+    }
+    if (!two && h) {  // keys past lk
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { x[r] = -INFINITY; y[r] = -INFINITY; }
+    }
+
+    // running maximum (NaN scores are skipped, as fmax does)
+    float mt = x[0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, x[r]), y[r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mnew = fmaxf(m, mt);
+    const bool grow = mnew > m;
+    if (__any(grow)) {
+      const float alpha = grow ? exp_ref_nonpos(m - mnew) : 1.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[0][r] *= alpha; acc[1][r] *= alpha; acc[2][r] *= alpha; acc[3][r] *= alpha;
+        lacc[r] *= alpha;
+      }
+      m = grow ? mnew : m;
+    }
+
+    // probabilities of the lane's 32-key block, in key order
+    uint32_t v[32];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
+        v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+      }
+    // p >= 0 or NaN, so the bit patterns order as the values and a NaN
+    // orders above every finite one
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
+    const uint32_t byte = scale_byte_from_amax<F_E2M1>(amax);
+    uint32_t pk[Fmt<F_E2M1>::W];
+    encode_f32<F_E2M1>(v, scale_operand(byte), pk);
+    if (byte == 0xFFu) {
+#pragma unroll
+      for (int e = 0; e < Fmt<F_E2M1>::W; ++e) pk[e] = 0u;
+    }
+    const i32x8_t pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int dd = 32 * T + col;
+      const i32x8_t va = load_v_operand<VF>(vsh + dd * VP, h);
+      acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[T], VF, 4, 0,
+                                                               (int)vsc[2 * dd + h], 0, (int)byte);
+    }
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 4, 4, 0, 127, 0,
+                                                           (int)byte);
+
+    const int blk = 2 * j + h;
+    if (pc != nullptr && qvalid && blk < nbk) {
+      const int64_t b = ((int64_t)bh * lq + qrow) * nbk + blk;
+      *reinterpret_cast<u32x4_t*>(pc + 16 * b) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+      ps[b] = (uint8_t)byte;
+    }
+  }
+
+  if (!qvalid) return;
+  const float l = lacc[0];
+  const int64_t row = (int64_t)bh * lq + qrow;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * T + 8 * g + 4 * h;
+      float r4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y = acc[T][4 * g + e] / l;
+        r4[e] = y != y ? __uint_as_float(0x7FC00000u) : y;
+      }
+      if constexpr (OUT_BF16) {
+        u32x2_t w;
+        w[0] = f32_to_bf16_rne(r4[0]) | (f32_to_bf16_rne(r4[1]) << 16);
+        w[1] = f32_to_bf16_rne(r4[2]) | (f32_to_bf16_rne(r4[3]) << 16);
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + row * kD + d0) = w;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(o) + row * kD + d0) =
+            make_float4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    }
+  if (h == 0) {
+    if (row_max) row_max[row] = m;
+    if (row_sum) row_sum[row] = l;
+  }
+}
+
+template <int VF>
+hipError_t launch_vf(bool out_bf16, const void* q, const void* k, const void* vc,
+                     const uint8_t* vs, int heads, int lq, int lk, float scale, void* o,
+                     float* rm, float* rs, uint8_t* pc, uint8_t* ps, hipStream_t st) {
+  const int qtiles = (lq + kRows - 1) / kRows;
+  const dim3 grid((unsigned)(heads * qtiles)), block(256);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint8_t* v8 = static_cast<const uint8_t*>(vc);
+  if (out_bf16)
+    hipLaunchKernelGGL((attention_fwd_mx<VF, true>), grid, block, 0, st, q16, k16, v8, vs, lq, lk,
+                       scale, qtiles, o, rm, rs, pc, ps);
+  else
+    hipLaunchKernelGGL((attention_fwd_mx<VF, false>), grid, block, 0, st, q16, k16, v8, vs, lq,
+                       lk, scale, qtiles, o, rm, rs, pc, ps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(int v_fmt, bool out_bf16, const void* q, const void* k,
+                            const void* v_codes, const uint8_t* v_scales, int heads, int lq,
+                            int lk, float scale, void* o, float* row_max, float* row_sum,
+                            void* p_codes, uint8_t* p_scales, hipStream_t st) {
+  uint8_t* pc = static_cast<uint8_t*>(p_codes);
+  switch (v_fmt) {
+    case F_E4M3:
+      return launch_vf<0>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
+                          row_sum, pc, p_scales, st);
+    case F_E2M3:
+      return launch_vf<2>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
+                          row_sum, pc, p_scales, st);
+    case F_E3M2:
+      return launch_vf<3>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
+                          row_sum, pc, p_scales, st);
+    case F_E2M1:
+      return launch_vf<4>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
+                          row_sum, pc, p_scales, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxk

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mx_exp.h"
 #include "mx_formats.h"
 #include "mx_hw.h"
 #include "mx_kernels.h"
@@ -508,40 +509,9 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Exp-then-quantize probabilities: one wavefront per row.
-// exp_fixed is the fp32 op sequence of the library's contract: Cody-Waite
-// reduction (Cody and Waite, "Software Manual for the Elementary
-// Functions", 1980) with ln2 split into a 16-bit head and a tail, a degree-7
-// Taylor polynomial by Horner's rule with fused multiply-adds, and scaling by
-// exact power-of-two products.  Constants: log2(e), ln2 and 1/k! rounded to
-// fp32; head = ln2's fp32 significand cut to 16 bits, tail = fp32(ln2 - head).
+// Exp-then-quantize probabilities: one wavefront per row (exp_ref_nonpos is
+// the fixed fp32 exp sequence, in mx_exp.h).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_nonpos(float d) {
-  // d is s - rowmax, so d <= 0 (or -inf); NaN rows never get here.  The
-  // reduction runs on max(d, -104): from there the product below already
-  // rounds to +0, which is the exact result for every d < -104 too.
-  const float kLog2e = 0x1.715476p+0f;
-  const float kLn2Hi = 0x1.62e400p-1f;
-  const float kLn2Lo = 0x1.7f7d1cp-20f;
-  const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
-              k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
-  const float dc = fmaxf(d, -104.0f);
-  const float nf = __builtin_rintf(dc * kLog2e);
-  float r = __builtin_fmaf(-nf, kLn2Hi, dc);
-  r = __builtin_fmaf(-nf, kLn2Lo, r);
-  float p = k7;
-  p = __builtin_fmaf(p, r, k6);
-  p = __builtin_fmaf(p, r, k5);
-  p = __builtin_fmaf(p, r, k4);
-  p = __builtin_fmaf(p, r, k3);
-  p = __builtin_fmaf(p, r, k2);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  // p * 2^n with one rounding (n in [-150, 0]; subnormal results rounded to
-  // nearest even), the same value as exact power-of-two pre-scaling
-  return __builtin_ldexpf(p, (int)nf);
-}
-
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -563,7 +533,7 @@ __device__ __forceinline__ void probs_block(const uint32_t (&sv)[32], float m, i
   uint32_t v[32];
   if (kind == 0) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_nonpos(__uint_as_float(sv[k]) - m));
+    for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_ref_nonpos(__uint_as_float(sv[k]) - m));
   } else {
 #pragma unroll
     for (int k = 0; k < 32; ++k) v[k] = (sv[k] == 0x7F800000u) ? 0x7FC00000u : 0u;

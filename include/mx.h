@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 1
+#define MX_ABI_VERSION 2
 #define MX_BLOCK 32
 
 typedef enum {
@@ -143,6 +143,51 @@ mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype,
 mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
                               int64_t rows, int64_t cols, void *codes,
                               uint8_t *scales, void *stream);
+
+/* Attention forward with exp-then-quantize E2M1 probabilities ("EFQ-
+ * Softmax" explainer, "Does it change FlashAttention?" and the stage table:
+ * the online-softmax row maximum, the rescaling of earlier sums, the high-
+ * precision accumulation and the final normalization are those of
+ * FlashAttention; the probabilities are exp() of the shifted scores
+ * quantized to block-scaled E2M1, and that one E2M1 operand feeds both the
+ * PV numerator and the denominator).  Per head and query row:
+ *   s = q . k in fp32 (bf16 products, fp32 matrix-core accumulation),
+ *   t = fp32(s * scale);
+ *   keys are taken 64 at a time: m_new = max(m, max t over the tile) (NaN
+ *   scores are skipped by the maximum); if m_new > m the running sums are
+ *   multiplied by exp(m - m_new); p = exp(t - m_new) with the fp32 exp of
+ *   mx_softmax_quantize; p is quantized per 32 keys to E2M1 by the rules
+ *   above (a NaN p gives a 0xFF block, which makes the row's output NaN);
+ *   the numerator adds P * V, the denominator adds P * 1, both from the
+ *   decoded E2M1 codes, in fp32;
+ *   o = numerator / denominator, rounded to out_dtype (NaN canonical).
+ * Arguments:
+ *   v_fmt     element format of V: MX_FP8_E4M3, MX_FP6_E2M3, MX_FP6_E3M2
+ *             or MX_FP4_E2M1 (MX_ERR_UNSUPPORTED otherwise)
+ *   block     32
+ *   q         [heads, lq, d] bf16;  k [heads, lk, d] bf16
+ *   v_codes, v_scales   V transposed, [heads, d, lk], quantized with
+ *             mx_quantize(v_fmt) (blocks of 32 keys): codes [heads, d,
+ *             lk/32, bpb], scales [heads, d, lk/32]
+ *   heads, lq, lk, d    d must be 128; lk > 0 and a multiple of 32;
+ *             heads == 0 or lq == 0 is a no-op
+ *   scale     score multiplier (typically 1/sqrt(d)), any fp32
+ *   o         [heads, lq, d] of out_dtype
+ *   row_max, row_sum    [heads, lq] fp32: the final m and denominator; may
+ *             be NULL
+ *   p_codes, p_scales   [heads, lq, lk/32, 16] and [heads, lq, lk/32]: the
+ *             E2M1 probability blocks exactly as they entered the PV
+ *             product (relative to the running maximum of their tile); both
+ *             NULL (normal use) or both set
+ * q, k, o, v_codes and p_codes must be 16-byte aligned.  Inputs are read
+ * only; nothing may overlap an output.  Asynchronous on `stream`. */
+mx_status mx_attention_fwd(mx_format v_fmt, int block, const void *q,
+                           const void *k, const void *v_codes,
+                           const uint8_t *v_scales, int64_t heads, int64_t lq,
+                           int64_t lk, int64_t d, float scale,
+                           mx_dtype out_dtype, void *o, float *row_max,
+                           float *row_sum, void *p_codes, uint8_t *p_scales,
+                           void *stream);
 
 #ifdef __cplusplus
 }

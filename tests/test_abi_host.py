@@ -27,7 +27,7 @@ def mx():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mx_quantize", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize",
-              "mx_buffer_sizes", "mx_status_str", "mx_abi_version"):
+              "mx_buffer_sizes", "mx_status_str", "mx_abi_version", "mx_attention_fwd"):
         assert f in names
 
 
@@ -50,7 +50,7 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 1
+    assert mx.mx_abi_version() == 2
     for s in range(0, 7):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
@@ -120,3 +120,36 @@ def test_generic_exmy_formats_host_checks(mx):
         assert mx.mx_quantize(bad, 32, 0, A, 4, 32, A, A, None, stream=0) == UNSUP
     assert mx.mx_softmax_quantize(mx.MX_EXMY(2, 1), 32, A, 4, 32, A, A, stream=0) == UNSUP
     assert mx.mx_quantize(mx.MX_EXMY(2, 2), 32, 0, None, 4, 32, A, A, None, stream=0) == NULL
+
+
+def test_attention_argument_errors(mx):
+    A = 1 << 20  # a fake 16-byte-aligned address; nothing is launched
+    OK, NULL, SHAPE, ALIGN, UNSUP = 0, 1, 2, 3, 4
+    E4M3, E2M3, E3M2, E2M1, AXS6 = mx.MX_FP8_E4M3, mx.MX_FP6_E2M3, mx.MX_FP6_E3M2, \
+        mx.MX_FP4_E2M1, mx.MX_AXS6
+
+    def call(v_fmt=E4M3, block=32, q=A, k=A, vc=A, vs=A, heads=2, lq=64, lk=128, d=128,
+             out=mx.MX_BF16, o=A, pc=None, ps=None):
+        return mx.mx_attention_fwd(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out, o,
+                                   None, None, pc, ps, stream=0)
+
+    assert call(v_fmt=AXS6) == UNSUP
+    assert call(v_fmt=mx.MX_EXMY(2, 3)) == UNSUP
+    assert call(block=16) == UNSUP
+    assert call(d=64) == UNSUP
+    assert call(out=7) == UNSUP
+    assert call(lk=0) == SHAPE
+    assert call(lk=48) == SHAPE
+    assert call(lq=-1) == SHAPE
+    assert call(heads=-1) == SHAPE
+    assert call(pc=A) == NULL           # probability codes without their scales
+    assert call(q=None) == NULL
+    assert call(vs=None) == NULL
+    assert call(q=A + 8) == ALIGN
+    assert call(o=A + 4) == ALIGN
+    assert call(pc=A + 8, ps=A) == ALIGN
+    # empty work is a no-op even with NULL pointers
+    assert call(heads=0, q=None, k=None, vc=None, vs=None, o=None) == OK
+    assert call(lq=0, q=None, k=None, vc=None, vs=None, o=None) == OK
+    for f in (E4M3, E2M3, E3M2, E2M1):
+        assert call(v_fmt=f, heads=0) == OK

@@ -1,0 +1,233 @@
+"""Fused attention forward with E2M1 probabilities (mx_attention_fwd) against
+the CPU oracle, through the C ABI.
+
+Inputs the oracle and the kernel share: q and k as bf16 bits, V^T quantized
+by the *oracle* (its codes are uploaded; nothing expected comes from the
+GPU).  Two kinds of scores:
+* exact: q and k hold multiples of 1/4 in [-3, 3], so every product and
+  partial sum of q . k (d = 128) is exact in fp32 whatever the
+  accumulation order; t = fp32(s * scale) is then the same number on both
+  sides, and the probability blocks, the scale bytes and the row maxima
+  must agree bit for bit;
+* natural: bf16 N(0, 1) q and k; the fp32 matrix-core sum may differ from
+  the oracle's correctly rounded score in the last bits, which can move a
+  probability across an E2M1 rounding boundary; such blocks are counted
+  and their effect is bounded exactly from the two sets of codes.
+Output bound (matching probability blocks): with A >= max over keys of |v|,
+    |o - o_ref| <= (c_V + g) A + (g + 2^-24) |o_ref| (+ 2^-7 |o_ref| in bf16)
+where g = (lk/8 + 2 ntiles + 2) 2^-24 covers the fp32 additions of group
+sums and the rescalings, and c_V = 2^-10 for E4M3 V (the matrix core's
+truncation inside groups of 8 FP8 products), 0 for FP6/FP4 V.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import oracle
+from block_scaled_bit_amd import workloads
+from gpu_util import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+V_FORMATS = {"e4m3": oracle.FP8_E4M3, "e2m3": oracle.FP6_E2M3, "e3m2": oracle.FP6_E3M2,
+             "e2m1": oracle.FP4_E2M1}
+D = 128
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_scaled_bit_amd as m
+    return m
+
+
+def bf16(x):
+    return workloads.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def exact_qk(rng, heads, lq, lk):
+    q = rng.integers(-12, 13, (heads, lq, D)).astype(np.float32) / 4
+    k = rng.integers(-12, 13, (heads, lk, D)).astype(np.float32) / 4
+    return bf16(q), bf16(k)
+
+
+def natural_qk(rng, heads, lq, lk):
+    return (bf16(rng.standard_normal((heads, lq, D))),
+            bf16(rng.standard_normal((heads, lk, D))))
+
+
+def v_input(rng, heads, lk, fmt):
+    v = (rng.standard_normal((heads, lk, D)) * np.exp2(rng.integers(-3, 4, (1, 1, D)))).astype(
+        np.float32)
+    vt = np.ascontiguousarray(v.transpose(0, 2, 1))
+    codes, scales, _ = oracle.quantize(fmt, vt)
+    return codes, scales
+
+
+def vhat_absmax(fmt, codes, scales, heads, lk):
+    """Upper bound of max over keys of |decoded V| per (head, d): the
+    format's largest finite magnitude times the block scale."""
+    top = brute.finite_grid(fmt).max()
+    s = scales.reshape(heads, D, lk // 32).astype(np.float64)
+    return (top * np.exp2(s - 127)).max(-1)
+
+
+def run_gpu(mx, fmt, q, k, vc, vs, scale, out_dtype):
+    heads, lq, _ = q.shape
+    lk = k.shape[1]
+    o, rm, rs, pc, ps = mx.attention_fwd(to_dev(q), to_dev(k), to_dev(vc), to_dev(vs), fmt,
+                                         scale=scale, out_dtype=out_dtype, stats=True, probs=True)
+    torch.cuda.synchronize()
+    return (to_host(o), to_host(rm), to_host(rs), to_host(pc).reshape(heads, lq, lk // 32, 16),
+            to_host(ps).reshape(heads, lq, lk // 32))
+
+
+def out_bound(fmt, lk, vmax, o_ref, bf16_out):
+    ntiles = -(-lk // 64)
+    g = (lk / 8 + 2 * ntiles + 2) * 2.0 ** -24
+    c = 2.0 ** -10 if fmt == oracle.FP8_E4M3 else 0.0
+    ao = np.abs(o_ref)
+    b = (c + g) * vmax[:, None, :] + (g + 2.0 ** -24) * ao
+    if bf16_out:
+        b = b + 2.0 ** -7 * ao
+    return b
+
+
+def as_f64(o, bf16_out):
+    return workloads.bf16_bits_to_f32(o).astype(np.float64) if bf16_out else o.astype(np.float64)
+
+
+@pytest.mark.parametrize("vname", list(V_FORMATS))
+@pytest.mark.parametrize("shape", [(2, 200, 416), (1, 1, 32), (3, 128, 64), (1, 33, 96)])
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_exact_scores_parity(mx, vname, shape, out):
+    fmt = V_FORMATS[vname]
+    heads, lq, lk = shape
+    rng = np.random.default_rng(zlib.crc32(repr((vname, shape, out)).encode()))
+    q, k = exact_qk(rng, heads, lq, lk)
+    vc, vs = v_input(rng, heads, lk, fmt)
+    scale = np.float32(D ** -0.5)
+    bf = out == "bf16"
+    od = oracle.BF16 if bf else oracle.FP32
+    o_ref, rm_ref, rs_ref, pc_ref, ps_ref = oracle.attention_fwd(fmt, q, k, vc, vs, scale, 64, od)
+    o, rm, rs, pc, ps = run_gpu(mx, fmt, q, k, vc, vs, scale,
+                                torch.bfloat16 if bf else torch.float32)
+    assert np.array_equal(ps, ps_ref), "probability scale bytes"
+    assert np.array_equal(pc, pc_ref), "probability codes"
+    assert np.array_equal(rm, rm_ref)  # by value (a zero maximum may differ in sign)
+    assert np.all(np.abs(rs.astype(np.float64) - rs_ref) <= 2.0 ** -20 * rs_ref)
+    ref = as_f64(o_ref, bf)
+    got = as_f64(o, bf)
+    vmax = vhat_absmax(fmt, vc, vs, heads, lk)
+    bound = out_bound(fmt, lk, vmax, ref, bf)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+@pytest.mark.parametrize("vname", ["e4m3", "e2m3"])
+def test_natural_scores(mx, vname):
+    fmt = V_FORMATS[vname]
+    heads, lq, lk = 2, 256, 512
+    rng = np.random.default_rng(7)
+    q, k = natural_qk(rng, heads, lq, lk)
+    vc, vs = v_input(rng, heads, lk, fmt)
+    scale = np.float32(D ** -0.5)
+    o_ref, rm_ref, rs_ref, pc_ref, ps_ref = oracle.attention_fwd(fmt, q, k, vc, vs, scale, 64,
+                                                                 oracle.FP32)
+    o, rm, rs, pc, ps = run_gpu(mx, fmt, q, k, vc, vs, scale, torch.float32)
+    same_block = np.all(pc == pc_ref, axis=-1) & (ps == ps_ref)
+    assert same_block.mean() > 0.999, same_block.mean()
+    # decoded E2M1 probabilities of both sides
+    g = brute.grid(oracle.FP4_E2M1)
+
+    def decode(pcodes, pscales):
+        nib = np.stack([pcodes & 15, pcodes >> 4], -1).reshape(pcodes.shape[:-1] + (32,))
+        return g[nib & 7] * np.exp2(pscales.astype(np.float64) - 127)[..., None]
+
+    dp = np.abs(decode(pc, ps) - decode(pc_ref, ps_ref)).reshape(heads, lq, lk)
+    vmax = vhat_absmax(fmt, vc, vs, heads, lk)
+    ref = o_ref.astype(np.float64)
+    bound = out_bound(fmt, lk, vmax, ref, False) + 1e-5 * vmax[:, None, :]
+    # a probability that moved by dp changes the numerator by at most
+    # dp (|v| + |o|) and the denominator by dp (rescale factors are <= 1)
+    flip = dp.sum(-1)[..., None] * (vmax[:, None, :] + np.abs(ref))
+    bound = bound + flip / np.maximum(rs_ref.astype(np.float64) - dp.sum(-1), 1e-30)[..., None]
+    err = np.abs(o.astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+def test_equal_scores_give_the_mean_of_v(mx):
+    # q = 0: every probability is exp(0) = 1, o = the plain mean of decoded V
+    rng = np.random.default_rng(3)
+    heads, lq, lk = 2, 40, 160
+    q = bf16(np.zeros((heads, lq, D)))
+    k = bf16(rng.standard_normal((heads, lk, D)))
+    vc, vs = v_input(rng, heads, lk, oracle.FP6_E2M3)
+    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP6_E2M3, q, k, vc, vs, 0.125, torch.float32)
+    vt = oracle.dequantize(oracle.FP6_E2M3, vc, vs, None, heads * D, lk, oracle.FP32)
+    want = vt.reshape(heads, D, lk).astype(np.float64).mean(-1)
+    assert np.allclose(o, np.broadcast_to(want[:, None, :], o.shape), rtol=1e-6, atol=1e-7)
+    assert np.all(rs == lk) and np.all(rm == 0.0)
+
+
+def test_one_dominant_key_gives_its_v_row(mx):
+    rng = np.random.default_rng(4)
+    heads, lq, lk = 1, 64, 256
+    qf = np.zeros((heads, lq, D), np.float32)
+    qf[..., 0] = 1.0
+    kf = rng.uniform(-1, 1, (heads, lk, D)).astype(np.float32)
+    kf[0, 200, 0] = 120.0
+    vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
+    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP8_E4M3, bf16(qf), bf16(kf), vc, vs, 1.0,
+                                torch.float32)
+    vt = oracle.dequantize(oracle.FP8_E4M3, vc, vs, None, heads * D, lk, oracle.FP32)
+    assert np.array_equal(o[0], np.broadcast_to(vt.reshape(D, lk)[:, 200], (lq, D)))
+    assert np.all(rm == 120.0) and np.all(rs == 1.0)
+
+
+def test_nan_score_poisons_its_row_only(mx):
+    rng = np.random.default_rng(5)
+    heads, lq, lk = 1, 64, 128
+    qf = rng.standard_normal((heads, lq, D)).astype(np.float32)
+    qf[0, 9, 17] = np.nan
+    q, k = bf16(qf), bf16(rng.standard_normal((heads, lk, D)))
+    vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
+    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP8_E4M3, q, k, vc, vs, 0.1, torch.bfloat16)
+    _, _, _, pc_ref, ps_ref = oracle.attention_fwd(oracle.FP8_E4M3, q, k, vc, vs, 0.1, 64,
+                                                   oracle.BF16)
+    assert np.all(o[0, 9] == 0x7FC0)  # canonical bf16 NaN
+    assert np.all(ps[0, 9] == 0xFF) and np.all(ps_ref[0, 9] == 0xFF)
+    others = np.delete(np.arange(lq), 9)
+    assert np.all(np.isfinite(workloads.bf16_bits_to_f32(o[0, others])))
+
+
+def test_full_size_sampled_rows(mx):
+    """32 heads x 4096 queries x 4096 keys, d = 128 (the attention-score
+    workload), E4M3 V, bf16 output, on natural scores: sampled rows against
+    the oracle (each row depends only on its own query)."""
+    heads, lq, lk = 32, 4096, 4096
+    rng = np.random.default_rng(11)
+    qd = torch.randn(heads, lq, D, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    kd = torch.randn(heads, lk, D, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    q, k = to_host(qd), to_host(kd)
+    vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
+    scale = np.float32(D ** -0.5)
+    o, rm, rs = mx.attention_fwd(qd, kd, to_dev(vc), to_dev(vs), "mxfp8", scale=scale,
+                                 out_dtype=torch.bfloat16, stats=True)
+    o, rm, rs = to_host(o), to_host(rm), to_host(rs)
+    vmax_all = vhat_absmax(oracle.FP8_E4M3, vc, vs, heads, lk)
+    for h, i in [(0, 0), (5, 1234), (17, 4095), (31, 2048), (12, 77)]:
+        o_ref, rm_ref, rs_ref, _, _ = oracle.attention_fwd(
+            oracle.FP8_E4M3, q[h:h + 1, i:i + 1], k[h:h + 1], vc.reshape(heads, -1)[h:h + 1],
+            vs.reshape(heads, -1)[h:h + 1], scale, 64, oracle.FP32)
+        ref = o_ref[0, 0].astype(np.float64)
+        got = workloads.bf16_bits_to_f32(o[h, i]).astype(np.float64)
+        vmax = vmax_all[h]
+        # natural scores: allow the probability-flip slack of a few blocks
+        tol = (2.0 ** -10 + 1e-4) * vmax + 2.0 ** -7 * np.abs(ref) + 0.01 * vmax
+        assert np.all(np.abs(got - ref) <= tol), (h, i)
+        assert abs(rm[h, i] - rm_ref[0, 0]) <= 1e-5 * max(1.0, abs(rm_ref[0, 0]))
