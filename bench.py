@@ -30,6 +30,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E datasheet peak, GB/s
+# fp32 vector issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz, in 10^12 lane-operations per second
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30
 METRIC = "MX quantize+pack GB/s and % of HBM peak, bf16 14336×4096 → MXFP6 E2M3"
@@ -194,6 +197,10 @@ def secondary(mx, steps):
     record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
     del sd, c, sc
 
+    # the same scores inside a fused attention forward: 32 heads x 4096
+    # queries x 4096 keys, d = 128, bf16 q/k, V^T in MXFP8, bf16 output
+    res.update(attention_line(mx, k))
+
     # layer-by-layer conversion of a synthetic dense decoder (4 layers,
     # hidden 4096, MLP 14336, 1024-wide k/v): weights already on the GPU, and
     # again from pinned host memory (that rate includes the PCIe upload)
@@ -234,6 +241,39 @@ def secondary(mx, steps):
     ms = time_launches(lambda i: mx.mx_quantize(0, 32, 1, xsm, 128, 256, cc, s1, None, stream), 1, k, 3)
     record("quantize_e2m3_weights_small", ms, 131072, 25600, "weights_small fp32 128x256 (launch-bound)")
     return res
+
+
+def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
+    """Fused attention forward with E2M1 probabilities (one launch)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q = torch.randn(heads, lq, d, generator=g, device="cuda").to(torch.bfloat16)
+    kk = torch.randn(heads, lk, d, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(heads, lk, d, generator=g, device="cuda")
+    vc, vs = mx.quantize_v(v, "mxfp8")
+    o = torch.empty(heads, lq, d, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    scale = d ** -0.5
+
+    def step(i):
+        st = mx.mx_attention_fwd(mx.MX_FP8_E4M3, 32, q, kk, vc, vs, heads, lq, lk, d, scale,
+                                 mx.MX_BF16, o, None, None, None, None, stream)
+        if st:
+            raise mx.MxError(st, "mx_attention_fwd")
+
+    ms = time_launches(step, 1, max(10, k // 4), 5)
+    flops = 4.0 * heads * lq * lk * d
+    scores = heads * lq * lk
+    # fp32 VALU operations the method fixes per score: the scaling, the
+    # shift, exp_ref's 14 and the block maximum = 17; the chip issues
+    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz of them per second
+    ops = 17.0 * scores
+    return {"attention_fwd_e2m1_p_mxfp8_v": {
+        "us": round(ms * 1e3, 2), "TFLOPs": round(flops / ms / 1e9, 1),
+        "Gscores_per_s": round(scores / ms / 1e6, 1),
+        "valu_frac": round(ops / ms / 1e9 / VALU_PEAK_TOPS, 4),
+        "workload": f"{heads} heads x {lq} queries x {lk} keys, d {d}, bf16 q/k, MXFP8 V^T, "
+                    "bf16 out"}}
 
 
 def cpu_baseline(x_np, gpu_codes, gpu_scales, passes=3):

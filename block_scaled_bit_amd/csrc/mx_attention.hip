@@ -49,55 +49,118 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glob_void_t;
 
 constexpr int kD = 128;              // head dimension
 constexpr int kTile = 64;            // keys per online-softmax step
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;   // queries per workgroup
-constexpr int kKPitch = 2 * kD + 16; // bytes per K row in LDS (16 B of padding
-                                     // keep the 16-B row reads conflict-free)
+constexpr int kKBytes = kTile * 2 * kD;  // one K tile in LDS: 64 rows of 256 B
 
-// V operand: instruction format code (0 E4M3, 2 E2M3, 3 E3M2, 4 E2M1) ->
-// packed bytes per 32 values and the LDS row pitch (two blocks + padding)
-template <int VF>
-constexpr int v_bpb() { return VF == 0 ? 32 : (VF == 4 ? 16 : 24); }
-template <int VF>
-constexpr int v_pitch() { return 2 * v_bpb<VF>() + 16; }
+// LDS layouts.  Tiles arrive by direct global->LDS loads, where lane i of
+// a wave writes the 16-byte slot i of a contiguous run (a 12-byte load
+// fills the first 12 bytes of its slot), so conflict-free reads come from
+// XOR-swizzling the slot order inside a row instead of padding.
+//   K: row r (key), 16-B chunk L (8 values of one row) in slot L ^ (r % 16).
+//   V^T, two blocks of row d: E4M3 4 chunks of 16 B, E2M3/E3M2 4 chunks of
+//      12 B (half a block each), chunk L in slot L ^ ((d / 2) % 4); E2M1 2
+//      chunks of 16 B, chunk L in slot L ^ ((d / 4) % 2).
+template <int VF> struct VTile;
+template <> struct VTile<0> {
+  static constexpr int BPB = 32, CH = 16, CPR = 4;
+  __device__ static int swz(int d) { return (d >> 1) & 3; }
+};
+template <> struct VTile<2> {
+  static constexpr int BPB = 24, CH = 12, CPR = 4;
+  __device__ static int swz(int d) { return (d >> 1) & 3; }
+};
+template <> struct VTile<3> : VTile<2> {};
+template <> struct VTile<4> {
+  static constexpr int BPB = 16, CH = 16, CPR = 2;
+  __device__ static int swz(int d) { return (d >> 2) & 1; }
+};
 
 // The A operand (V^T row d, lane half h) of the block-scaled MFMA from the
 // LDS copy of the tile's two blocks of that row.
 template <int VF>
-__device__ __forceinline__ i32x8_t load_v_operand(const uint8_t* row, int h) {
+__device__ __forceinline__ i32x8_t load_v_operand(const uint8_t* vt, int d, int h) {
+  using L = VTile<VF>;
+  const uint8_t* row = vt + d * L::CPR * 16;
+  const int z = L::swz(d);
   i32x8_t a = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (VF == 0) {
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(row + 16 * h);
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(row + 32 + 16 * h);
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(row + 16 * (h ^ z));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(row + 16 * ((2 + h) ^ z));
     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
     a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
   } else if constexpr (VF == 4) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + 16 * h);
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + 16 * (h ^ z));
     a[0] = w[0]; a[1] = w[1]; a[2] = w[2]; a[3] = w[3];
   } else {
-    const u32x2_t w0 = *reinterpret_cast<const u32x2_t*>(row + 24 * h);
-    const u32x2_t w1 = *reinterpret_cast<const u32x2_t*>(row + 24 * h + 8);
-    const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(row + 24 * h + 16);
-    a[0] = w0[0]; a[1] = w0[1]; a[2] = w1[0]; a[3] = w1[1]; a[4] = w2[0]; a[5] = w2[1];
+    const u32x3_t lo = *reinterpret_cast<const u32x3_t*>(row + 16 * ((2 * h) ^ z));
+    const u32x3_t hi = *reinterpret_cast<const u32x3_t*>(row + 16 * ((2 * h + 1) ^ z));
+    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = hi[0]; a[4] = hi[1]; a[5] = hi[2];
   }
   return a;
 }
 
+// One direct global->LDS load: lane i of the wave writes its 16 (12) bytes
+// at l + 16 i (12 i); l must be the same for the whole wave.
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load12(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)l, 12, 0, 0);
+}
+
+// Start the direct loads of key tile jt into one LDS buffer (K rows past lk
+// and a missing second V block re-read valid rows; their products are
+// masked).  Every wave issues 4 K and up to 2 V instructions.
+template <int VF>
+__device__ __forceinline__ void issue_tile(uint8_t* ksb, uint8_t* vsb, const uint16_t* k,
+                                           const uint8_t* vc, int bh, int lk, int nbk, int jt,
+                                           int wave, int lane) {
+  using L = VTile<VF>;
+  const int key0 = jt * kTile, kb0 = key0 / 32;
+  const bool two = kb0 + 1 < nbk;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int c = (4 * n + wave) * 64 + lane;
+    const int r = c >> 4, chunk = (c & 15) ^ (r & 15);
+    const int key = min(key0 + r, lk - 1);
+    lds_load16(k + ((int64_t)bh * lk + key) * kD + 8 * chunk, ksb + (4 * n + wave) * 64 * 16);
+  }
+  constexpr int nchunks = kD * L::CPR;
+#pragma unroll
+  for (int n = 0; n < (nchunks + 255) / 256; ++n) {
+    if ((4 * n + wave) * 64 < nchunks) {
+      const int c = (4 * n + wave) * 64 + lane;
+      const int d = c / L::CPR;
+      int chunk = (c - d * L::CPR) ^ L::swz(d);
+      if (!two && chunk >= L::CPR / 2) chunk -= L::CPR / 2;
+      const uint8_t* src = vc + (((int64_t)bh * kD + d) * nbk + kb0) * L::BPB + L::CH * chunk;
+      uint8_t* dst = vsb + (4 * n + wave) * 64 * 16;
+      if constexpr (L::CH == 16) lds_load16(src, dst);
+      else lds_load12(src, dst);
+    }
+  }
+}
+
 template <int VF, bool OUT_BF16>
-__global__ __launch_bounds__(256) void attention_fwd_mx(
+__global__ __launch_bounds__(256, 2) void attention_fwd_mx(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int lq, int lk,
     float scale, int qtiles, void* __restrict__ o, float* __restrict__ row_max,
     float* __restrict__ row_sum, uint8_t* __restrict__ pc, uint8_t* __restrict__ ps) {
-  constexpr int BPB = v_bpb<VF>();
-  constexpr int VP = v_pitch<VF>();
-  constexpr int IPD = 2 * BPB / 8;  // 8-byte items per V^T row of a tile
-  __shared__ __align__(16) uint8_t ks[kTile * kKPitch];
-  __shared__ __align__(16) uint8_t vsh[kD * VP];
-  __shared__ uint8_t vsc[kD * 2];
+  using VL = VTile<VF>;
+  // two buffers as separate LDS objects: the compiler can then tell that
+  // loads streaming into one never alias reads of the other
+  __shared__ __align__(16) uint8_t ks0[kKBytes], ks1[kKBytes];
+  __shared__ __align__(16) uint8_t vsh0[kD * VL::CPR * 16], vsh1[kD * VL::CPR * 16];
+  __shared__ uint8_t vsc0[kD * 2], vsc1[kD * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -137,35 +200,35 @@ __global__ __launch_bounds__(256) void attention_fwd_mx(
   float m = -INFINITY;
   const i32x8_t ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int key0 = j * kTile;
-    const int kb0 = key0 / 32;
+  // V^T scale bytes of tile jt for row d = tid (tid < 128): the second
+  // address repeats the first when the tile has one block, so both loads
+  // are unconditional and nothing waits for them before they are stored
+  auto scale_ptr = [&](int jt) { return vs + ((int64_t)bh * kD + tid) * nbk + 2 * jt; };
+  issue_tile<VF>(ks0, vsh0, k, vc, bh, lk, nbk, 0, wave, lane);
+  if (tid < kD) {
+    const uint8_t* sp = scale_ptr(0);
+    vsc0[2 * tid] = sp[0];
+    vsc0[2 * tid + 1] = 1 < nbk ? sp[1] : (uint8_t)127;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // one 64-key tile: compute from (kt, vt, st) while tile j + 1 streams
+  // into (kn, vn, sn)
+  auto step = [&](int j, const uint8_t* kt, const uint8_t* vt, const uint8_t* st, uint8_t* kn,
+                  uint8_t* vn, uint8_t* sn) __attribute__((always_inline)) {
+    const int kb0 = 2 * j;
     const bool two = kb0 + 1 < nbk;  // false only for a last tile of 32 keys
-    __syncthreads();
-    // K tile: 64 rows of 256 B in 16-B chunks (rows past lk read as zero)
-    for (int c = tid; c < kTile * 16; c += 256) {
-      const int r = c >> 4, cc = c & 15;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (key0 + r < lk)
-        w = *reinterpret_cast<const u32x4_t*>(k + ((int64_t)bh * lk + key0 + r) * kD + 8 * cc);
-      *reinterpret_cast<u32x4_t*>(ks + r * kKPitch + 16 * cc) = w;
+    const bool two_next = kb0 + 3 < nbk;
+    uint8_t sc_lo = 0, sc_hi = 0;
+    if (j + 1 < ntiles) {
+      issue_tile<VF>(kn, vn, k, vc, bh, lk, nbk, j + 1, wave, lane);
+      if (tid < kD) {
+        const uint8_t* sp = scale_ptr(j + 1);
+        sc_lo = sp[0];
+        sc_hi = sp[two_next ? 1 : 0];
+      }
     }
-    // V^T tile: 128 rows (d) of two blocks, 8-B items; a missing second
-    // block reads as zero codes under scale 1
-    for (int c = tid; c < kD * IPD; c += 256) {
-      const int dd = c / IPD, it = c - dd * IPD;
-      u32x2_t w = {0u, 0u};
-      if (two || it < IPD / 2)
-        w = *reinterpret_cast<const u32x2_t*>(vc + (((int64_t)bh * kD + dd) * nbk + kb0) * BPB +
-                                              8 * it);
-      *reinterpret_cast<u32x2_t*>(vsh + dd * VP + 8 * it) = w;
-    }
-    if (tid < kD) {
-      const uint8_t* sp = vs + ((int64_t)bh * kD + tid) * nbk + kb0;
-      vsc[2 * tid] = sp[0];
-      vsc[2 * tid + 1] = two ? sp[1] : (uint8_t)127;
-    }
-    __syncthreads();
 
     // S^T for keys key0 .. +31 (s0) and key0+32 .. +63 (s1)
     f32x16_t s0, s1;
@@ -173,9 +236,10 @@ __global__ __launch_bounds__(256) void attention_fwd_mx(
     for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(ks + col * kKPitch + 128 * h + 16 * i);
-      const u32x4_t a1 =
-          *reinterpret_cast<const u32x4_t*>(ks + (32 + col) * kKPitch + 128 * h + 16 * i);
+      // logical chunk 8h + i of rows col and 32 + col (same r % 16)
+      const int pch = ((8 * h + i) ^ (col & 15)) * 16;
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kt + col * 256 + pch);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kt + (32 + col) * 256 + pch);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), qf[i], s0, 0,
                                                    0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qf[i], s1, 0,
@@ -191,16 +255,28 @@ __global__ __launch_bounds__(256) void attention_fwd_mx(
       x[r] = __uint_as_float(sw[0]) * scale;
       y[r] = __uint_as_float(sw[1]) * scale;
     }
-    if (!two && h) {  // keys past lk
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { x[r] = -INFINITY; y[r] = -INFINITY; }
-    }
+    const bool dead = !two && h;  // the block past lk of a 32-key last tile
 
-    // running maximum (NaN scores are skipped, as fmax does)
+    // Tile maximum with NaN propagation (IEEE maximum): a NaN score, or an
+    // infinite running maximum, sends the whole wave through the careful
+    // path below; otherwise no shifted score can be NaN.
     float mt = x[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, x[r]), y[r]);
+    for (int r = 0; r < 16; ++r)
+      mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mt, x[r]), y[r]);
+    mt = dead ? -INFINITY : mt;
     {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool careful = __any(mt != mt || !(__builtin_fabsf(fmaxf(m, mt)) < INFINITY));
+    if (careful) {
+      // the maximum the method defines skips NaN scores
+      mt = x[0];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, x[r]), y[r]);
+      mt = dead ? -INFINITY : mt;
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -212,40 +288,50 @@ __global__ __launch_bounds__(256) void attention_fwd_mx(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         acc[0][r] *= alpha; acc[1][r] *= alpha; acc[2][r] *= alpha; acc[3][r] *= alpha;
-        lacc[r] *= alpha;
       }
+      lacc[0] *= alpha;  // the other 15 copies of l are never read
       m = grow ? mnew : m;
     }
 
     // probabilities of the lane's 32-key block, in key order
     uint32_t v[32];
+    if (careful) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
-        v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
-      }
+        for (int e = 0; e < 4; ++e) {
+          v[8 * g + e] = __float_as_uint(exp_ref_nonpos<true>(x[4 * g + e] - m));
+          v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos<true>(y[4 * g + e] - m));
+        }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
+          v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+        }
+    }
     // p >= 0 or NaN, so the bit patterns order as the values and a NaN
     // orders above every finite one
     uint32_t amax = 0u;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
-    const uint32_t byte = scale_byte_from_amax<F_E2M1>(amax);
+    uint32_t byte = scale_byte_from_amax<F_E2M1>(amax);
     uint32_t pk[Fmt<F_E2M1>::W];
     encode_f32<F_E2M1>(v, scale_operand(byte), pk);
-    if (byte == 0xFFu) {
+    const bool zero = dead || byte == 0xFFu;  // no codes (a NaN block keeps 0xFF)
+    byte = dead ? 0u : byte;
 #pragma unroll
-      for (int e = 0; e < Fmt<F_E2M1>::W; ++e) pk[e] = 0u;
-    }
+    for (int e = 0; e < Fmt<F_E2M1>::W; ++e) pk[e] = zero ? 0u : pk[e];
     const i32x8_t pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const int dd = 32 * T + col;
-      const i32x8_t va = load_v_operand<VF>(vsh + dd * VP, h);
+      const i32x8_t va = load_v_operand<VF>(vt, dd, h);
       acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[T], VF, 4, 0,
-                                                               (int)vsc[2 * dd + h], 0, (int)byte);
+                                                               (int)st[2 * dd + h], 0, (int)byte);
     }
     lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 4, 4, 0, 127, 0,
                                                            (int)byte);
@@ -256,6 +342,18 @@ __global__ __launch_bounds__(256) void attention_fwd_mx(
       *reinterpret_cast<u32x4_t*>(pc + 16 * b) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
       ps[b] = (uint8_t)byte;
     }
+    if (j + 1 < ntiles && tid < kD) {
+      sn[2 * tid] = sc_lo;
+      sn[2 * tid + 1] = two_next ? sc_hi : (uint8_t)127;
+    }
+    // the next tile has landed (own loads) and nobody reads this buffer
+    // any more (barrier) before it is refilled
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, ks0, vsh0, vsc0, ks1, vsh1, vsc1);
+    if (j + 1 < ntiles) step(j + 1, ks1, vsh1, vsc1, ks0, vsh0, vsc0);
   }
 
   if (!qvalid) return;

@@ -14,17 +14,19 @@
 
 namespace mxk {
 
-// exp(d) for d <= 0 (shifted scores), -inf -> 0, NaN -> NaN.  The reduction
+// exp(d) for d <= 0 (shifted scores) and d = -inf (-> 0).  The reduction
 // runs on max(d, -104): from there the product below already rounds to +0,
-// which is the exact result for every d < -104 too.  The clamp is written as
-// a comparison so that a NaN d passes through.
+// which is the exact result for every d < -104 too.  kNaN: a NaN d gives NaN
+// (the clamp is then a comparison, one more instruction); otherwise the
+// caller guarantees d is not NaN.
+template <bool kNaN = false>
 __device__ __forceinline__ float exp_ref_nonpos(float d) {
   const float kLog2e = 0x1.715476p+0f;
   const float kLn2Hi = 0x1.62e400p-1f;
   const float kLn2Lo = 0x1.7f7d1cp-20f;
   const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
               k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
-  const float dc = d < -104.0f ? -104.0f : d;
+  const float dc = kNaN ? (d < -104.0f ? -104.0f : d) : __builtin_fmaxf(d, -104.0f);
   const float nf = __builtin_rintf(dc * kLog2e);
   float r = __builtin_fmaf(-nf, kLn2Hi, dc);
   r = __builtin_fmaf(-nf, kLn2Lo, r);
