@@ -165,7 +165,7 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void* q, const void
   if (block != MX_BLOCK || d != 128 || !dtype_ok(out_dtype)) return MX_ERR_UNSUPPORTED;
   if (heads < 0 || lq < 0 || lk <= 0 || lk % MX_BLOCK != 0) return MX_ERR_SHAPE;
   // int32 indices inside the kernel: every per-head and grid count must fit
-  if (heads > INT32_MAX || lq > INT32_MAX - 128 || lk > INT32_MAX) return MX_ERR_SHAPE;
+  if (heads > INT32_MAX || lq > INT32_MAX - 128 || lk > (1 << 24)) return MX_ERR_SHAPE;
   if (heads * ((lq + 127) / 128) > INT32_MAX) return MX_ERR_SHAPE;
   if (heads > 0 && lq > 0 && (heads * lq > INT64_MAX / (2 * 128 * 16) ||
                               heads * lk > INT64_MAX / (2 * 128 * 16)))

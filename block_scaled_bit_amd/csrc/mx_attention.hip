@@ -116,38 +116,69 @@ __device__ __forceinline__ void lds_load12(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)l, 12, 0, 0);
 }
 
-// Start the direct loads of key tile jt into one LDS buffer (K rows past lk
-// and a missing second V block re-read valid rows; their products are
-// masked).  Every wave issues 4 K and up to 2 V instructions.
+// Direct loads of one key tile into one LDS buffer.  Each wave issues 4 K
+// and up to 2 V instructions; every lane's address is a fixed per-lane
+// offset plus a per-tile base that is the same for the whole wave, so the
+// per-tile cost is scalar arithmetic.  K rows past lk and a missing second
+// V block (a last tile of 32 keys) re-read valid data; the kernel masks
+// their products.
 template <int VF>
-__device__ __forceinline__ void issue_tile(uint8_t* ksb, uint8_t* vsb, const uint16_t* k,
-                                           const uint8_t* vc, int bh, int lk, int nbk, int jt,
-                                           int wave, int lane) {
+struct TileLoader {
   using L = VTile<VF>;
-  const int key0 = jt * kTile, kb0 = key0 / 32;
-  const bool two = kb0 + 1 < nbk;
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int c = (4 * n + wave) * 64 + lane;
-    const int r = c >> 4, chunk = (c & 15) ^ (r & 15);
-    const int key = min(key0 + r, lk - 1);
-    lds_load16(k + ((int64_t)bh * lk + key) * kD + 8 * chunk, ksb + (4 * n + wave) * 64 * 16);
+  const uint8_t* kh;  // this head's K
+  const uint8_t* vh;  // this head's V^T codes
+  int64_t vrows64;    // bytes of 64 V^T rows
+  uint32_t koff;      // lane's K byte offset inside a tile (instruction 0)
+  uint32_t voff;      // lane's V byte offset (instruction 0, tile 0)
+  uint32_t vhalf;     // bytes back to the first block when the lane's chunk is in the second
+  int lk, nbk, wave;
+
+  __device__ void init(const uint16_t* k, const uint8_t* vc, int bh, int lk_, int nbk_,
+                       int wave_, int lane) {
+    lk = lk_;
+    nbk = nbk_;
+    wave = wave_;
+    kh = reinterpret_cast<const uint8_t*>(k) + (int64_t)bh * lk * (2 * kD);
+    vh = vc + (int64_t)bh * kD * nbk * L::BPB;
+    vrows64 = (int64_t)64 * nbk * L::BPB;
+    // K chunk c = 64 (4n + wave) + lane: row 16n + 4 wave + lane / 16, slot
+    // lane % 16, logical chunk slot ^ (row % 16) (n does not change it)
+    const int r0 = 4 * wave + (lane >> 4);
+    koff = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ (r0 & 15)));
+    // V chunk c = 64 (4n + wave) + lane: row c / CPR, slot c % CPR (n adds
+    // 64 rows and does not change the swizzle)
+    const int c0 = wave * 64 + lane;
+    const int d0 = c0 / L::CPR;
+    const int ch = (c0 - d0 * L::CPR) ^ L::swz(d0);
+    voff = (uint32_t)(d0 * nbk * L::BPB + L::CH * ch);
+    vhalf = ch >= L::CPR / 2 ? (uint32_t)(L::CH * (L::CPR / 2)) : 0u;
   }
-  constexpr int nchunks = kD * L::CPR;
+
+  __device__ __forceinline__ void issue(uint8_t* ksb, uint8_t* vsb, int jt) const {
+    const int key0 = jt * kTile, kb0 = 2 * jt;
+    const bool two = kb0 + 1 < nbk;
+    const uint8_t* kt = kh + (int64_t)key0 * (2 * kD);
 #pragma unroll
-  for (int n = 0; n < (nchunks + 255) / 256; ++n) {
-    if ((4 * n + wave) * 64 < nchunks) {
-      const int c = (4 * n + wave) * 64 + lane;
-      const int d = c / L::CPR;
-      int chunk = (c - d * L::CPR) ^ L::swz(d);
-      if (!two && chunk >= L::CPR / 2) chunk -= L::CPR / 2;
-      const uint8_t* src = vc + (((int64_t)bh * kD + d) * nbk + kb0) * L::BPB + L::CH * chunk;
-      uint8_t* dst = vsb + (4 * n + wave) * 64 * 16;
-      if constexpr (L::CH == 16) lds_load16(src, dst);
-      else lds_load12(src, dst);
+    for (int n = 0; n < 4; ++n) {
+      // rows 16n.. of a 32-key last tile do not exist for n >= 2: re-read
+      // rows 16n - 32..
+      const uint8_t* base = kt + (int64_t)(n * 16 - ((!two && n >= 2) ? 32 : 0)) * (2 * kD);
+      lds_load16(base + koff, ksb + (4 * n + wave) * 64 * 16);
+    }
+    const uint32_t vo = two ? voff : voff - vhalf;
+    const uint8_t* vt = vh + (int64_t)kb0 * L::BPB;
+    constexpr int nchunks = kD * L::CPR;
+#pragma unroll
+    for (int n = 0; n < (nchunks + 255) / 256; ++n) {
+      if ((4 * n + wave) * 64 < nchunks) {
+        const uint8_t* src = vt + n * vrows64 + vo;
+        uint8_t* dst = vsb + (4 * n + wave) * 64 * 16;
+        if constexpr (L::CH == 16) lds_load16(src, dst);
+        else lds_load12(src, dst);
+      }
     }
   }
-}
+};
 
 template <int VF, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
@@ -203,8 +234,12 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
   // V^T scale bytes of tile jt for row d = tid (tid < 128): the second
   // address repeats the first when the tile has one block, so both loads
   // are unconditional and nothing waits for them before they are stored
-  auto scale_ptr = [&](int jt) { return vs + ((int64_t)bh * kD + tid) * nbk + 2 * jt; };
-  issue_tile<VF>(ks0, vsh0, k, vc, bh, lk, nbk, 0, wave, lane);
+  const uint8_t* vs_head = vs + (int64_t)bh * kD * nbk;
+  const uint32_t soff = (uint32_t)(tid * nbk);
+  auto scale_ptr = [&](int jt) { return vs_head + 2 * jt + soff; };
+  TileLoader<VF> loader;
+  loader.init(k, vc, bh, lk, nbk, wave, lane);
+  loader.issue(ks0, vsh0, 0);
   if (tid < kD) {
     const uint8_t* sp = scale_ptr(0);
     vsc0[2 * tid] = sp[0];
@@ -222,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
     const bool two_next = kb0 + 3 < nbk;
     uint8_t sc_lo = 0, sc_hi = 0;
     if (j + 1 < ntiles) {
-      issue_tile<VF>(kn, vn, k, vc, bh, lk, nbk, j + 1, wave, lane);
+      loader.issue(kn, vn, j + 1);
       if (tid < kD) {
         const uint8_t* sp = scale_ptr(j + 1);
         sc_lo = sp[0];

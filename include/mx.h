@@ -169,8 +169,8 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
  *   v_codes, v_scales   V transposed, [heads, d, lk], quantized with
  *             mx_quantize(v_fmt) (blocks of 32 keys): codes [heads, d,
  *             lk/32, bpb], scales [heads, d, lk/32]
- *   heads, lq, lk, d    d must be 128; lk > 0 and a multiple of 32;
- *             heads == 0 or lq == 0 is a no-op
+ *   heads, lq, lk, d    d must be 128; lk > 0, a multiple of 32 and at
+ *             most 2^24; heads == 0 or lq == 0 is a no-op
  *   scale     score multiplier (typically 1/sqrt(d)), any fp32
  *   o         [heads, lq, d] of out_dtype
  *   row_max, row_sum    [heads, lq] fp32: the final m and denominator; may
