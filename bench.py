@@ -40,19 +40,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
 
 
+# the translation unit the headline kernel is compiled from
+HEADLINE_SOURCES = ("mx_exp.h", "mx_formats.h", "mx_hw.h", "mx_kernels.h", "mx_kernels.hip")
+
+
 def source_digest() -> str:
-    """Digest of the kernel sources with comments and whitespace removed, so
-    that counter figures stay attached to the code they were taken on."""
+    """Digest of the headline kernel's sources with comments and whitespace
+    removed, so that counter figures stay attached to the code they were
+    taken on."""
     import re
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name)) as f:
-                text = f.read()
-            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-            text = re.sub(r"//[^\n]*", " ", text)
-            text = " ".join(text.split())
-            h.update(name.encode() + b"\0" + text.encode())
+    for name in sorted(HEADLINE_SOURCES):
+        with open(os.path.join(CSRC, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 
@@ -338,6 +342,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of the headline's byte count")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="only time the fused attention forward (for profiling it alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -354,6 +360,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.only_attention:
+        print(json.dumps(attention_line(mx, args.steps)), flush=True)
         return
 
     x = workloads.linear_weight()
