@@ -1,12 +1,12 @@
 // mx_attention.hip -- attention forward with exp-then-quantize E2M1
 // probabilities on gfx950 (device code and its launcher).
 //
-// Method: "EFQ-Softmax: exp-free E2M1 probabilities" (explainer), sections
-// "Does it change FlashAttention?" and the stage table: the online softmax
-// keeps a running row maximum, rescales the earlier sums when it grows,
-// accumulates in high precision and normalizes once; the probabilities are
-// exp() of the shifted scores, quantized to block-scaled E2M1 (MXFP4) for
-// the PV product, and the same E2M1 block feeds the denominator.
+// Method: the EFQ-Softmax explainer, sections "Does it change
+// FlashAttention?" and the stage table: the online softmax keeps a running
+// row maximum, rescales the earlier sums when it grows, accumulates in wide
+// registers and divides once; the probabilities are exp() of the shifted
+// scores, quantized to block-scaled E2M1 (MXFP4) for the PV product, and
+// the same E2M1 block is summed for the normalizer.
 //
 // Work split: one workgroup of 4 waves per (head, 128 queries); each wave
 // owns 32 queries and walks the keys in tiles of 64:
@@ -19,8 +19,8 @@
 //   O^T += V^T * P^T         4 block-scaled 32x32x64 MFMAs (V in E4M3,
 //                            E2M3, E3M2 or E2M1, P in E2M1)
 //   l   += 1 * P^T           one more block-scaled MFMA with an all-ones A
-// so the probabilities never leave registers and both the numerator and the
-// denominator consume the same E2M1 operand.  K and V^T tiles are staged in
+// so the probabilities never leave registers and the PV product and the
+// normalizing sum consume the same E2M1 operand.  K and V^T tiles are staged in
 // LDS once per workgroup and shared by its 4 waves.
 //
 // Operand layouts (checked on the hardware by the library's probe tests):

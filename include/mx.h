@@ -146,11 +146,12 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
 
 /* Attention forward with exp-then-quantize E2M1 probabilities ("EFQ-
  * Softmax" explainer, "Does it change FlashAttention?" and the stage table:
- * the online-softmax row maximum, the rescaling of earlier sums, the high-
- * precision accumulation and the final normalization are those of
- * FlashAttention; the probabilities are exp() of the shifted scores
- * quantized to block-scaled E2M1, and that one E2M1 operand feeds both the
- * PV numerator and the denominator).  Per head and query row:
+ * FlashAttention's online softmax is kept as it is -- a running row
+ * maximum, partial sums rescaled when it grows, wide accumulators, one
+ * division at the end -- while the probabilities become exp() of the
+ * shifted scores quantized to block-scaled E2M1, and that one E2M1 operand
+ * is used for the PV product and for the normalizing sum).  Per head and
+ * query row:
  *   s = q . k in fp32 (bf16 products, fp32 matrix-core accumulation),
  *   t = fp32(s * scale);
  *   keys are taken 64 at a time: m_new = max(m, max t over the tile) (NaN
