@@ -78,8 +78,12 @@ def _load():
     lib.mxref_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P]
     lib.mxref_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I,
                                         I, P, P, P, P, P]
+    lib.mxref_attention_fwd_efq.argtypes = lib.mxref_attention_fwd.argtypes
+    lib.mxref_efq_block.argtypes = [P, P]
+    lib.mxref_efq_quantize_block.argtypes = [P, P]
     for f in ("mxref_quantize", "mxref_dequantize", "mxref_fake_quantize",
-              "mxref_softmax_probs", "mxref_softmax_quantize", "mxref_attention_fwd"):
+              "mxref_softmax_probs", "mxref_softmax_quantize", "mxref_attention_fwd",
+              "mxref_attention_fwd_efq", "mxref_efq_block", "mxref_efq_quantize_block"):
         getattr(lib, f).restype = I
     return lib
 
@@ -200,10 +204,28 @@ def softmax_quantize(fmt: int, s: np.ndarray):
     return codes.reshape(rows, nbr, BYTES_PER_BLOCK[fmt]), scales.reshape(rows, nbr)
 
 
+def efq_block(d) -> tuple:
+    """EFQ reading on 32 shifted scores (fp32): (scale byte, codes[32])."""
+    d = np.ascontiguousarray(np.asarray(d, np.float32).reshape(BLOCK))
+    codes = np.zeros(BLOCK, np.int32)
+    byte = _lib.mxref_efq_block(_ptr(d), _ptr(codes))
+    return byte, codes
+
+
+def efq_quantize_block(d) -> tuple:
+    """EFQ reading on 32 shifted scores: (scale byte, 16 packed bytes)."""
+    d = np.ascontiguousarray(np.asarray(d, np.float32).reshape(BLOCK))
+    packed = np.zeros(16, np.uint8)
+    byte = _lib.mxref_efq_quantize_block(_ptr(d), _ptr(packed))
+    return byte, packed
+
+
 def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,
-                  v_scales: np.ndarray, scale: float, kv_tile: int = 64, out_dtype: int = FP32):
+                  v_scales: np.ndarray, scale: float, kv_tile: int = 64, out_dtype: int = FP32,
+                  efq: bool = False):
     """Attention forward with E2M1 probabilities (online softmax over
-    `kv_tile` keys at a time).  q [heads, lq, d] and k [heads, lk, d] are
+    `kv_tile` keys at a time); efq=True uses the exp-free EFQ reading for the
+    probability blocks instead of exp-then-quantize.  q [heads, lq, d] and k [heads, lk, d] are
     bf16 bit patterns; v_codes/v_scales are V^T ([heads, d, lk]) quantized
     with ``quantize(v_fmt, .)``.  Returns (o [heads, lq, d], row_max,
     row_sum [heads, lq], p_codes [heads, lq, lk/32, 16], p_scales
@@ -224,9 +246,10 @@ def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,
     row_sum = np.empty((heads, lq), np.float32)
     p_codes = np.empty((heads, lq, nbk, 16), np.uint8)
     p_scales = np.empty((heads, lq, nbk), np.uint8)
-    rc = _lib.mxref_attention_fwd(v_fmt, BLOCK, _ptr(q), _ptr(k), _ptr(v_codes), _ptr(v_scales),
-                                  heads, lq, lk, d, float(scale), kv_tile, out_dtype, _ptr(o),
-                                  _ptr(row_max), _ptr(row_sum), _ptr(p_codes), _ptr(p_scales))
+    fn = _lib.mxref_attention_fwd_efq if efq else _lib.mxref_attention_fwd
+    rc = fn(v_fmt, BLOCK, _ptr(q), _ptr(k), _ptr(v_codes), _ptr(v_scales), heads, lq, lk, d,
+            float(scale), kv_tile, out_dtype, _ptr(o), _ptr(row_max), _ptr(row_sum),
+            _ptr(p_codes), _ptr(p_scales))
     if rc:
         raise ValueError("oracle attention_fwd: bad arguments")
     return o, row_max, row_sum, p_codes, p_scales

@@ -528,12 +528,70 @@ static double bf16_value(uint16_t b) {
   return (double)fv;
 }
 
-int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
-                        const uint16_t *k, const uint8_t *v_codes,
-                        const uint8_t *v_scales, int64_t heads, int64_t lq,
-                        int64_t lk, int64_t d, float scale, int kv_tile,
-                        int out_dtype, void *o, float *row_max,
-                        float *row_sum, uint8_t *p_codes, uint8_t *p_scales) {
+/* ------------------------------------------------------------------ */
+/* EFQ's exp-free probability block ([EFQ] article, the paragraph that  */
+/* starts "Concretely", and the stage table): no exp(); an exponent-     */
+/* only scale chosen from the block's local maximum normalizes the      */
+/* shifted scores, and one affine rule maps them to nonnegative E2M1    */
+/* codes.  The pages give no constants, so the rule below is a reading  */
+/* (PARITY UNPINNED by the pages; only its stated properties are       */
+/* tested):                                                             */
+/*   u = fp32(d * log2 e)             shifted score in powers of two    */
+/*   U = max u; byte = clamp(floor(U) - 2 + 127, 0, 254)                */
+/*                                    (the MX rule applied to 2^U)      */
+/*   w = u - (byte - 127)             exact in fp32                     */
+/*   code = trunc(clamp(fp32(fma(w, 2, 2.5)), 0, 7.5))                  */
+/* so w = 0, 1, 2 (values X, 2X, 4X) give the even codes 2, 4, 6 that   */
+/* hold exactly those values, and the odd codes take the log-domain     */
+/* midpoints.  A NaN shifted score poisons the block (0xFF, codes 0);   */
+/* U = -inf gives byte 0 and codes 0.                                   */
+/* ------------------------------------------------------------------ */
+int mxref_efq_block(const float *dv, int *codes) {
+  const float LOG2E = 0x1.715476p+0f;
+  float u[BLOCK], U = -INFINITY;
+  int k, byte, E;
+  for (k = 0; k < BLOCK; k++)
+    if (isnan(dv[k])) {
+      for (k = 0; k < BLOCK; k++) codes[k] = 0;
+      return 0xFF;
+    }
+  for (k = 0; k < BLOCK; k++) {
+    u[k] = dv[k] * LOG2E;
+    if (u[k] > U) U = u[k];
+  }
+  if (U == -INFINITY) {
+    for (k = 0; k < BLOCK; k++) codes[k] = 0;
+    return 0;
+  }
+  E = (int)floorf(U);
+  byte = E - 2 + 127;
+  if (byte < 0) byte = 0;
+  if (byte > 254) byte = 254;
+  for (k = 0; k < BLOCK; k++) {
+    float w = u[k] - (float)(byte - 127);
+    float x = fmaf(w, 2.0f, 2.5f);
+    if (!(x > 0.0f)) x = 0.0f;
+    if (x > 7.5f) x = 7.5f;
+    codes[k] = (int)x;
+  }
+  return byte;
+}
+
+int mxref_efq_quantize_block(const float *dv, uint8_t *packed) {
+  fmt_t fp;
+  int codes[BLOCK], byte;
+  get_fmt(MXREF_FP4_E2M1, &fp);
+  byte = mxref_efq_block(dv, codes);
+  pack_block(&fp, codes, packed);
+  return byte;
+}
+
+static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
+                         const uint16_t *k, const uint8_t *v_codes,
+                         const uint8_t *v_scales, int64_t heads, int64_t lq,
+                         int64_t lk, int64_t d, float scale, int kv_tile,
+                         int out_dtype, void *o, float *row_max,
+                         float *row_sum, uint8_t *p_codes, uint8_t *p_scales) {
   fmt_t fv, fp;
   int64_t h, i, j, c, kk, nbk;
   double *vhat = 0, *acc = 0;
@@ -590,12 +648,15 @@ int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
         }
         for (kk = j; kk < end; kk += BLOCK) {
           double pv[BLOCK], phat[BLOCK];
+          float dv[BLOCK];
           int codes[BLOCK], e, byte;
-          for (e = 0; e < BLOCK; e++) {
-            float dd = t[kk + e] - m;
-            pv[e] = (double)mxref_exp(dd);
+          for (e = 0; e < BLOCK; e++) dv[e] = t[kk + e] - m;
+          if (rule == 0) {
+            for (e = 0; e < BLOCK; e++) pv[e] = (double)mxref_exp(dv[e]);
+            byte = quantize_values(&fp, MXREF_FP4_E2M1, pv, codes);
+          } else {
+            byte = mxref_efq_block(dv, codes);
           }
-          byte = quantize_values(&fp, MXREF_FP4_E2M1, pv, codes);
           for (e = 0; e < BLOCK; e++)
             phat[e] = byte == 0xFF ? NAN
                                    : mxref_decode(MXREF_FP4_E2M1, codes[e]) *
@@ -617,4 +678,29 @@ int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
   free(acc);
   free(t);
   return 0;
+}
+
+int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
+                        const uint16_t *k, const uint8_t *v_codes,
+                        const uint8_t *v_scales, int64_t heads, int64_t lq,
+                        int64_t lk, int64_t d, float scale, int kv_tile,
+                        int out_dtype, void *o, float *row_max,
+                        float *row_sum, uint8_t *p_codes, uint8_t *p_scales) {
+  return attention_fwd(0, v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk,
+                       d, scale, kv_tile, out_dtype, o, row_max, row_sum,
+                       p_codes, p_scales);
+}
+
+/* the same forward with EFQ's exp-free probability blocks (a reading,
+ * parity unpinned by the pages; see mxref_efq_block) */
+int mxref_attention_fwd_efq(int v_fmt, int block, const uint16_t *q,
+                            const uint16_t *k, const uint8_t *v_codes,
+                            const uint8_t *v_scales, int64_t heads,
+                            int64_t lq, int64_t lk, int64_t d, float scale,
+                            int kv_tile, int out_dtype, void *o,
+                            float *row_max, float *row_sum, uint8_t *p_codes,
+                            uint8_t *p_scales) {
+  return attention_fwd(1, v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk,
+                       d, scale, kv_tile, out_dtype, o, row_max, row_sum,
+                       p_codes, p_scales);
 }

@@ -71,6 +71,18 @@ int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
                         int out_dtype, void *o, float *row_max,
                         float *row_sum, uint8_t *p_codes, uint8_t *p_scales);
 
+/* EFQ's exp-free probabilities (a reading; parity unpinned by the pages):
+ * the E2M1 codes of one block of 32 shifted scores, and the scale byte */
+int mxref_efq_block(const float *dv, int *codes);
+int mxref_efq_quantize_block(const float *dv, uint8_t *packed);
+int mxref_attention_fwd_efq(int v_fmt, int block, const uint16_t *q,
+                            const uint16_t *k, const uint8_t *v_codes,
+                            const uint8_t *v_scales, int64_t heads,
+                            int64_t lq, int64_t lk, int64_t d, float scale,
+                            int kv_tile, int out_dtype, void *o,
+                            float *row_max, float *row_sum, uint8_t *p_codes,
+                            uint8_t *p_scales);
+
 #ifdef __cplusplus
 }
 #endif
