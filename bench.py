@@ -248,7 +248,8 @@ def secondary(mx, steps):
 
 
 def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
-    """Fused attention forward with E2M1 probabilities (one launch)."""
+    """Fused attention forward with E2M1 probabilities (one launch), with
+    exp-then-quantize probabilities and with the exp-free EFQ reading."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(21)
     q = torch.randn(heads, lq, d, generator=g, device="cuda").to(torch.bfloat16)
@@ -259,25 +260,30 @@ def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
     stream = torch.cuda.current_stream().cuda_stream
     scale = d ** -0.5
 
-    def step(i):
-        st = mx.mx_attention_fwd(mx.MX_FP8_E4M3, 32, q, kk, vc, vs, heads, lq, lk, d, scale,
-                                 mx.MX_BF16, o, None, None, None, None, stream)
-        if st:
-            raise mx.MxError(st, "mx_attention_fwd")
-
-    ms = time_launches(step, 1, max(10, k // 4), 5)
+    out = {}
     flops = 4.0 * heads * lq * lk * d
     scores = heads * lq * lk
-    # fp32 VALU operations the method fixes per score: the scaling, the
-    # shift, exp_ref's 14 and the block maximum = 17; the chip issues
-    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz of them per second
-    ops = 17.0 * scores
-    return {"attention_fwd_e2m1_p_mxfp8_v": {
-        "us": round(ms * 1e3, 2), "TFLOPs": round(flops / ms / 1e9, 1),
-        "Gscores_per_s": round(scores / ms / 1e6, 1),
-        "valu_frac": round(ops / ms / 1e9 / VALU_PEAK_TOPS, 4),
-        "workload": f"{heads} heads x {lq} queries x {lk} keys, d {d}, bf16 q/k, MXFP8 V^T, "
-                    "bf16 out"}}
+    # fp32 VALU operations the method fixes per score -- exp-then-quantize:
+    # the scaling, the shift, exp_ref's 14 and the block maximum = 17;
+    # EFQ: the scaling, the shift, log2 e, the block maximum, the affine
+    # map (subtract, fma, clamp, convert) = 8.  The chip issues 256 CUs x 4
+    # SIMDs x 16 lanes x 2.4 GHz of them per second.
+    for name, fn, ops_per in (("attention_fwd_e2m1_p_mxfp8_v", mx.mx_attention_fwd, 17.0),
+                              ("attention_fwd_efq_e2m1_p_mxfp8_v", mx.mx_attention_fwd_efq, 8.0)):
+        def step(i, fn=fn):
+            st = fn(mx.MX_FP8_E4M3, 32, q, kk, vc, vs, heads, lq, lk, d, scale, mx.MX_BF16, o,
+                    None, None, None, None, stream)
+            if st:
+                raise mx.MxError(st, "attention forward")
+
+        ms = time_launches(step, 1, max(10, k // 4), 5)
+        out[name] = {
+            "us": round(ms * 1e3, 2), "TFLOPs": round(flops / ms / 1e9, 1),
+            "Gscores_per_s": round(scores / ms / 1e6, 1),
+            "valu_frac": round(ops_per * scores / ms / 1e9 / VALU_PEAK_TOPS, 4),
+            "workload": f"{heads} heads x {lq} queries x {lk} keys, d {d}, bf16 q/k, MXFP8 V^T, "
+                        "bf16 out"}
+    return out
 
 
 def cpu_baseline(x_np, gpu_codes, gpu_scales, passes=3):

@@ -17,7 +17,8 @@ import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
 __all__ = [
     "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
     "FORMATS", "MX_EXMY", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
-    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd", "quantize",
+    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd",
+    "mx_attention_fwd_efq", "quantize",
     "dequantize", "fake_quantize", "softmax_quantize", "quantize_v", "attention_fwd",
     "library_path",
 ]
@@ -72,8 +73,9 @@ def _load():
     lib.mx_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P, P]
     lib.mx_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I, P,
                                      P, P, P, P, P]
+    lib.mx_attention_fwd_efq.argtypes = lib.mx_attention_fwd.argtypes
     for f in ("mx_buffer_sizes", "mx_quantize", "mx_dequantize", "mx_fake_quantize",
-              "mx_softmax_quantize", "mx_attention_fwd"):
+              "mx_softmax_quantize", "mx_attention_fwd", "mx_attention_fwd_efq"):
         getattr(lib, f).restype = I
     return lib
 
@@ -159,6 +161,14 @@ def mx_attention_fwd(v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d, sc
                                  _ptr(v_scales), heads, lq, lk, d, float(scale), out_dtype, _ptr(o),
                                  _ptr(row_max), _ptr(row_sum), _ptr(p_codes), _ptr(p_scales),
                                  _stream(stream))
+
+
+def mx_attention_fwd_efq(v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d, scale,
+                         out_dtype, o, row_max, row_sum, p_codes, p_scales, stream=None) -> int:
+    return _lib.mx_attention_fwd_efq(_fmt(v_fmt), block, _ptr(q), _ptr(k), _ptr(v_codes),
+                                     _ptr(v_scales), heads, lq, lk, d, float(scale), out_dtype,
+                                     _ptr(o), _ptr(row_max), _ptr(row_sum), _ptr(p_codes),
+                                     _ptr(p_scales), _stream(stream))
 
 
 # ---------------------------------------------------------------------------
@@ -247,11 +257,12 @@ def quantize_v(v: torch.Tensor, fmt="mxfp8"):
 
 def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
                   v_scales: torch.Tensor, v_fmt="mxfp8", scale=None, out_dtype=torch.bfloat16,
-                  stats: bool = False, probs: bool = False):
+                  stats: bool = False, probs: bool = False, efq: bool = False):
     """Attention forward with E2M1 probabilities.  q [heads, lq, 128] and k
     [heads, lk, 128] bf16; V given as ``quantize_v`` returns it.  Returns o
     [heads, lq, 128]; with stats=True also (row_max, row_sum); with
-    probs=True also the E2M1 probability blocks (p_codes, p_scales)."""
+    probs=True also the E2M1 probability blocks (p_codes, p_scales).
+    efq=True: the exp-free EFQ probability rule (mx_attention_fwd_efq)."""
     f = _fmt(v_fmt)
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
         raise MxError(4, "attention_fwd needs bf16 q and k")
@@ -272,8 +283,10 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
     if probs:
         pc = torch.empty((heads, lq, lk // BLOCK, 16), dtype=torch.uint8, device=q.device)
         ps = torch.empty((heads, lq, lk // BLOCK), dtype=torch.uint8, device=q.device)
-    _check(mx_attention_fwd(f, BLOCK, q, k, v_codes, v_scales, heads, lq, lk, d, scale,
-                            _dtype_code(o), o, rm, rs, pc, ps), "mx_attention_fwd")
+    fn, name = (mx_attention_fwd_efq, "mx_attention_fwd_efq") if efq else \
+        (mx_attention_fwd, "mx_attention_fwd")
+    _check(fn(f, BLOCK, q, k, v_codes, v_scales, heads, lq, lk, d, scale, _dtype_code(o), o, rm,
+              rs, pc, ps), name)
     out = (o,)
     if stats:
         out += (rm, rs)

@@ -154,11 +154,13 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float* s, int64_t 
                                                static_cast<hipStream_t>(stream)));
 }
 
-mx_status mx_attention_fwd(mx_format v_fmt, int block, const void* q, const void* k,
-                           const void* v_codes, const uint8_t* v_scales, int64_t heads,
-                           int64_t lq, int64_t lk, int64_t d, float scale, mx_dtype out_dtype,
-                           void* o, float* row_max, float* row_sum, void* p_codes,
-                           uint8_t* p_scales, void* stream) {
+namespace {
+
+mx_status attention(bool efq, mx_format v_fmt, int block, const void* q, const void* k,
+                    const void* v_codes, const uint8_t* v_scales, int64_t heads, int64_t lq,
+                    int64_t lk, int64_t d, float scale, mx_dtype out_dtype, void* o,
+                    float* row_max, float* row_sum, void* p_codes, uint8_t* p_scales,
+                    void* stream) {
   if (!(v_fmt == MX_FP8_E4M3 || v_fmt == MX_FP6_E2M3 || v_fmt == MX_FP6_E3M2 ||
         v_fmt == MX_FP4_E2M1))
     return MX_ERR_UNSUPPORTED;
@@ -176,9 +178,30 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v_codes) || !aligned16(o) ||
       (p_codes && !aligned16(p_codes)))
     return MX_ERR_ALIGN;
-  return from_hip(mxk::launch_attention(v_fmt, out_dtype == MX_BF16, q, k, v_codes, v_scales,
-                                        (int)heads, (int)lq, (int)lk, scale, o, row_max, row_sum,
-                                        p_codes, p_scales, static_cast<hipStream_t>(stream)));
+  return from_hip(mxk::launch_attention(v_fmt, efq, out_dtype == MX_BF16, q, k, v_codes,
+                                        v_scales, (int)heads, (int)lq, (int)lk, scale, o, row_max,
+                                        row_sum, p_codes, p_scales,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+mx_status mx_attention_fwd(mx_format v_fmt, int block, const void* q, const void* k,
+                           const void* v_codes, const uint8_t* v_scales, int64_t heads,
+                           int64_t lq, int64_t lk, int64_t d, float scale, mx_dtype out_dtype,
+                           void* o, float* row_max, float* row_sum, void* p_codes,
+                           uint8_t* p_scales, void* stream) {
+  return attention(false, v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d, scale,
+                   out_dtype, o, row_max, row_sum, p_codes, p_scales, stream);
+}
+
+mx_status mx_attention_fwd_efq(mx_format v_fmt, int block, const void* q, const void* k,
+                               const void* v_codes, const uint8_t* v_scales, int64_t heads,
+                               int64_t lq, int64_t lk, int64_t d, float scale,
+                               mx_dtype out_dtype, void* o, float* row_max, float* row_sum,
+                               void* p_codes, uint8_t* p_scales, void* stream) {
+  return attention(true, v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d, scale,
+                   out_dtype, o, row_max, row_sum, p_codes, p_scales, stream);
 }
 
 }  // extern "C"

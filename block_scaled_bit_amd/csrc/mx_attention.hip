@@ -180,7 +180,7 @@ struct TileLoader {
   }
 };
 
-template <int VF, bool OUT_BF16>
+template <int VF, bool OUT_BF16, bool EFQ>
 __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int lq, int lk,
@@ -328,33 +328,69 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
       m = grow ? mnew : m;
     }
 
-    // probabilities of the lane's 32-key block, in key order
-    uint32_t v[32];
-    if (careful) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[8 * g + e] = __float_as_uint(exp_ref_nonpos<true>(x[4 * g + e] - m));
-          v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos<true>(y[4 * g + e] - m));
-        }
-    } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
-          v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
-        }
-    }
-    // p >= 0 or NaN, so the bit patterns order as the values and a NaN
-    // orders above every finite one
-    uint32_t amax = 0u;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
-    uint32_t byte = scale_byte_from_amax<F_E2M1>(amax);
+    uint32_t byte;
     uint32_t pk[Fmt<F_E2M1>::W];
-    encode_f32<F_E2M1>(v, scale_operand(byte), pk);
+    if constexpr (!EFQ) {
+      // probabilities of the lane's 32-key block, in key order
+      uint32_t v[32];
+      if (careful) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * g + e] = __float_as_uint(exp_ref_nonpos<true>(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos<true>(y[4 * g + e] - m));
+          }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+          }
+      }
+      // p >= 0 or NaN, so the bit patterns order as the values and a NaN
+      // orders above every finite one
+      uint32_t amax = 0u;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
+      byte = scale_byte_from_amax<F_E2M1>(amax);
+      encode_f32<F_E2M1>(v, scale_operand(byte), pk);
+    } else {
+      // EFQ reading, no exp: u = (t - m) log2 e; the MX scale rule on 2^max u;
+      // code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5)).  A NaN u
+      // (NaN score, or inf - inf) poisons the block through the
+      // NaN-propagating maximum.
+      const float kLog2e = 0x1.715476p+0f;
+      float u[32];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u[8 * g + e] = (x[4 * g + e] - m) * kLog2e;
+          u[8 * g + 4 + e] = (y[4 * g + e] - m) * kLog2e;
+        }
+      float U = u[0];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) U = __builtin_elementwise_maximum(U, u[e]);
+      // floor of max(U, -1000): every U below gives byte 0 as well
+      const int E = (int)__builtin_floorf(__builtin_fmaxf(U, -1000.0f));
+      const int b = min(max(E - Fmt<F_E2M1>::EMAX + 127, 0), 254);
+      const float shift = (float)(b - 127);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = __builtin_amdgcn_fmed3f(__builtin_fmaf(u[8 * j + e] - shift, 2.0f, 2.5f),
+                                                  0.0f, 7.5f);
+          w |= (uint32_t)c << (4 * e);
+        }
+        pk[j] = w;
+      }
+      byte = U != U ? 0xFFu : (uint32_t)b;
+    }
     const bool zero = dead || byte == 0xFFu;  // no codes (a NaN block keeps 0xFF)
     byte = dead ? 0u : byte;
 #pragma unroll
@@ -421,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_mx(
   }
 }
 
-template <int VF>
+template <int VF, bool EFQ>
 hipError_t launch_vf(bool out_bf16, const void* q, const void* k, const void* vc,
                      const uint8_t* vs, int heads, int lq, int lk, float scale, void* o,
                      float* rm, float* rs, uint8_t* pc, uint8_t* ps, hipStream_t st) {
@@ -431,37 +467,48 @@ hipError_t launch_vf(bool out_bf16, const void* q, const void* k, const void* vc
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint8_t* v8 = static_cast<const uint8_t*>(vc);
   if (out_bf16)
-    hipLaunchKernelGGL((attention_fwd_mx<VF, true>), grid, block, 0, st, q16, k16, v8, vs, lq, lk,
-                       scale, qtiles, o, rm, rs, pc, ps);
+    hipLaunchKernelGGL((attention_fwd_mx<VF, true, EFQ>), grid, block, 0, st, q16, k16, v8, vs,
+                       lq, lk, scale, qtiles, o, rm, rs, pc, ps);
   else
-    hipLaunchKernelGGL((attention_fwd_mx<VF, false>), grid, block, 0, st, q16, k16, v8, vs, lq,
+    hipLaunchKernelGGL((attention_fwd_mx<VF, false, EFQ>), grid, block, 0, st, q16, k16, v8, vs, lq,
                        lk, scale, qtiles, o, rm, rs, pc, ps);
   return hipGetLastError();
 }
 
+template <bool EFQ>
+hipError_t launch_rule(int v_fmt, bool out_bf16, const void* q, const void* k,
+                       const void* v_codes, const uint8_t* v_scales, int heads, int lq, int lk,
+                       float scale, void* o, float* row_max, float* row_sum, uint8_t* pc,
+                       uint8_t* ps, hipStream_t st) {
+  switch (v_fmt) {
+    case F_E4M3:
+      return launch_vf<0, EFQ>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o,
+                               row_max, row_sum, pc, ps, st);
+    case F_E2M3:
+      return launch_vf<2, EFQ>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o,
+                               row_max, row_sum, pc, ps, st);
+    case F_E3M2:
+      return launch_vf<3, EFQ>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o,
+                               row_max, row_sum, pc, ps, st);
+    case F_E2M1:
+      return launch_vf<4, EFQ>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o,
+                               row_max, row_sum, pc, ps, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_attention(int v_fmt, bool out_bf16, const void* q, const void* k,
+hipError_t launch_attention(int v_fmt, bool efq, bool out_bf16, const void* q, const void* k,
                             const void* v_codes, const uint8_t* v_scales, int heads, int lq,
                             int lk, float scale, void* o, float* row_max, float* row_sum,
                             void* p_codes, uint8_t* p_scales, hipStream_t st) {
   uint8_t* pc = static_cast<uint8_t*>(p_codes);
-  switch (v_fmt) {
-    case F_E4M3:
-      return launch_vf<0>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
-                          row_sum, pc, p_scales, st);
-    case F_E2M3:
-      return launch_vf<2>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
-                          row_sum, pc, p_scales, st);
-    case F_E3M2:
-      return launch_vf<3>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
-                          row_sum, pc, p_scales, st);
-    case F_E2M1:
-      return launch_vf<4>(out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale, o, row_max,
-                          row_sum, pc, p_scales, st);
-    default:
-      return hipErrorInvalidValue;
-  }
+  return efq ? launch_rule<true>(v_fmt, out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale,
+                                 o, row_max, row_sum, pc, p_scales, st)
+             : launch_rule<false>(v_fmt, out_bf16, q, k, v_codes, v_scales, heads, lq, lk, scale,
+                                  o, row_max, row_sum, pc, p_scales, st);
 }
 
 }  // namespace mxk

@@ -34,10 +34,11 @@ hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const 
                        hipStream_t st);
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
                                    void* codes, uint8_t* scales, hipStream_t st);
-// Attention forward with E2M1 probabilities; head dimension 128, v_fmt one
-// of E2M3, E3M2, E2M1, E4M3; row_max, row_sum, p_codes, p_scales may be NULL
+// Attention forward with E2M1 probabilities (efq: the exp-free EFQ reading
+// instead of exp-then-quantize); head dimension 128, v_fmt one of E2M3,
+// E3M2, E2M1, E4M3; row_max, row_sum, p_codes, p_scales may be NULL
 // (p_codes and p_scales together).
-hipError_t launch_attention(int v_fmt, bool out_bf16, const void* q, const void* k,
+hipError_t launch_attention(int v_fmt, bool efq, bool out_bf16, const void* q, const void* k,
                             const void* v_codes, const uint8_t* v_scales, int heads, int lq,
                             int lk, float scale, void* o, float* row_max, float* row_sum,
                             void* p_codes, uint8_t* p_scales, hipStream_t st);

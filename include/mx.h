@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 2
+#define MX_ABI_VERSION 3
 #define MX_BLOCK 32
 
 typedef enum {
@@ -189,6 +189,26 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void *q,
                            mx_dtype out_dtype, void *o, float *row_max,
                            float *row_sum, void *p_codes, uint8_t *p_scales,
                            void *stream);
+
+/* The same attention forward with EFQ's exp-free probability blocks ("EFQ-
+ * Softmax" explainer, the paragraph that starts "Concretely" and the stage
+ * table: no exp(); an exponent-only scale from the block's local maximum
+ * normalizes the shifted scores and one affine rule maps them to
+ * nonnegative E2M1 codes).  The page prints no constants; this library's
+ * reading, identical in the CPU reference:
+ *   u = fp32((t - m_new) * log2 e) for the block's 32 keys,
+ *   byte = clamp(floor(max u) - 2 + 127, 0, 254) (the MX rule on 2^max u),
+ *   code = trunc(clamp(fp32(fma(u - (byte - 127), 2, 2.5)), 0, 7.5)),
+ * so shifted scores at exact powers of two land on the even codes that hold
+ * those values; a NaN u gives a 0xFF block.  Everything else, arguments and
+ * errors included, is as in mx_attention_fwd. */
+mx_status mx_attention_fwd_efq(mx_format v_fmt, int block, const void *q,
+                               const void *k, const void *v_codes,
+                               const uint8_t *v_scales, int64_t heads,
+                               int64_t lq, int64_t lk, int64_t d, float scale,
+                               mx_dtype out_dtype, void *o, float *row_max,
+                               float *row_sum, void *p_codes,
+                               uint8_t *p_scales, void *stream);
 
 #ifdef __cplusplus
 }

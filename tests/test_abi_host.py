@@ -27,7 +27,8 @@ def mx():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mx_quantize", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize",
-              "mx_buffer_sizes", "mx_status_str", "mx_abi_version", "mx_attention_fwd"):
+              "mx_buffer_sizes", "mx_status_str", "mx_abi_version", "mx_attention_fwd",
+              "mx_attention_fwd_efq"):
         assert f in names
 
 
@@ -50,7 +51,7 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 2
+    assert mx.mx_abi_version() == 3
     for s in range(0, 7):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
@@ -130,8 +131,12 @@ def test_attention_argument_errors(mx):
 
     def call(v_fmt=E4M3, block=32, q=A, k=A, vc=A, vs=A, heads=2, lq=64, lk=128, d=128,
              out=mx.MX_BF16, o=A, pc=None, ps=None):
-        return mx.mx_attention_fwd(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out, o,
-                                   None, None, pc, ps, stream=0)
+        rc = mx.mx_attention_fwd(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out, o,
+                                 None, None, pc, ps, stream=0)
+        rc_efq = mx.mx_attention_fwd_efq(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out,
+                                         o, None, None, pc, ps, stream=0)
+        assert rc == rc_efq
+        return rc
 
     assert call(v_fmt=AXS6) == UNSUP
     assert call(v_fmt=mx.MX_EXMY(2, 3)) == UNSUP
@@ -140,6 +145,7 @@ def test_attention_argument_errors(mx):
     assert call(out=7) == UNSUP
     assert call(lk=0) == SHAPE
     assert call(lk=48) == SHAPE
+    assert call(lk=(1 << 24) + 32) == SHAPE
     assert call(lq=-1) == SHAPE
     assert call(heads=-1) == SHAPE
     assert call(pc=A) == NULL           # probability codes without their scales

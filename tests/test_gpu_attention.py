@@ -1,5 +1,6 @@
-"""Fused attention forward with E2M1 probabilities (mx_attention_fwd) against
-the CPU oracle, through the C ABI.
+"""Fused attention forward with E2M1 probabilities (mx_attention_fwd, and
+mx_attention_fwd_efq with the exp-free EFQ reading) against the CPU oracle,
+through the C ABI.
 
 Inputs the oracle and the kernel share: q and k as bf16 bits, V^T quantized
 by the *oracle* (its codes are uploaded; nothing expected comes from the
@@ -76,11 +77,12 @@ def vhat_absmax(fmt, codes, scales, heads, lk):
     return (top * np.exp2(s - 127)).max(-1)
 
 
-def run_gpu(mx, fmt, q, k, vc, vs, scale, out_dtype):
+def run_gpu(mx, fmt, q, k, vc, vs, scale, out_dtype, efq=False):
     heads, lq, _ = q.shape
     lk = k.shape[1]
     o, rm, rs, pc, ps = mx.attention_fwd(to_dev(q), to_dev(k), to_dev(vc), to_dev(vs), fmt,
-                                         scale=scale, out_dtype=out_dtype, stats=True, probs=True)
+                                         scale=scale, out_dtype=out_dtype, stats=True, probs=True,
+                                         efq=efq)
     torch.cuda.synchronize()
     return (to_host(o), to_host(rm), to_host(rs), to_host(pc).reshape(heads, lq, lk // 32, 16),
             to_host(ps).reshape(heads, lq, lk // 32))
@@ -101,21 +103,24 @@ def as_f64(o, bf16_out):
     return workloads.bf16_bits_to_f32(o).astype(np.float64) if bf16_out else o.astype(np.float64)
 
 
+@pytest.mark.parametrize("rule", ["exp", "efq"])
 @pytest.mark.parametrize("vname", list(V_FORMATS))
 @pytest.mark.parametrize("shape", [(2, 200, 416), (1, 1, 32), (3, 128, 64), (1, 33, 96)])
 @pytest.mark.parametrize("out", ["fp32", "bf16"])
-def test_exact_scores_parity(mx, vname, shape, out):
+def test_exact_scores_parity(mx, vname, shape, out, rule):
     fmt = V_FORMATS[vname]
     heads, lq, lk = shape
-    rng = np.random.default_rng(zlib.crc32(repr((vname, shape, out)).encode()))
+    efq = rule == "efq"
+    rng = np.random.default_rng(zlib.crc32(repr((vname, shape, out, rule)).encode()))
     q, k = exact_qk(rng, heads, lq, lk)
     vc, vs = v_input(rng, heads, lk, fmt)
     scale = np.float32(D ** -0.5)
     bf = out == "bf16"
     od = oracle.BF16 if bf else oracle.FP32
-    o_ref, rm_ref, rs_ref, pc_ref, ps_ref = oracle.attention_fwd(fmt, q, k, vc, vs, scale, 64, od)
+    o_ref, rm_ref, rs_ref, pc_ref, ps_ref = oracle.attention_fwd(fmt, q, k, vc, vs, scale, 64, od,
+                                                                 efq=efq)
     o, rm, rs, pc, ps = run_gpu(mx, fmt, q, k, vc, vs, scale,
-                                torch.bfloat16 if bf else torch.float32)
+                                torch.bfloat16 if bf else torch.float32, efq=efq)
     assert np.array_equal(ps, ps_ref), "probability scale bytes"
     assert np.array_equal(pc, pc_ref), "probability codes"
     assert np.array_equal(rm, rm_ref)  # by value (a zero maximum may differ in sign)
@@ -128,17 +133,19 @@ def test_exact_scores_parity(mx, vname, shape, out):
     assert np.all(err <= bound), float((err / bound).max())
 
 
+@pytest.mark.parametrize("rule", ["exp", "efq"])
 @pytest.mark.parametrize("vname", ["e4m3", "e2m3"])
-def test_natural_scores(mx, vname):
+def test_natural_scores(mx, vname, rule):
     fmt = V_FORMATS[vname]
     heads, lq, lk = 2, 256, 512
+    efq = rule == "efq"
     rng = np.random.default_rng(7)
     q, k = natural_qk(rng, heads, lq, lk)
     vc, vs = v_input(rng, heads, lk, fmt)
     scale = np.float32(D ** -0.5)
     o_ref, rm_ref, rs_ref, pc_ref, ps_ref = oracle.attention_fwd(fmt, q, k, vc, vs, scale, 64,
-                                                                 oracle.FP32)
-    o, rm, rs, pc, ps = run_gpu(mx, fmt, q, k, vc, vs, scale, torch.float32)
+                                                                 oracle.FP32, efq=efq)
+    o, rm, rs, pc, ps = run_gpu(mx, fmt, q, k, vc, vs, scale, torch.float32, efq=efq)
     same_block = np.all(pc == pc_ref, axis=-1) & (ps == ps_ref)
     assert same_block.mean() > 0.999, same_block.mean()
     # decoded E2M1 probabilities of both sides
@@ -160,21 +167,24 @@ def test_natural_scores(mx, vname):
     assert np.all(err <= bound), float((err / bound).max())
 
 
-def test_equal_scores_give_the_mean_of_v(mx):
-    # q = 0: every probability is exp(0) = 1, o = the plain mean of decoded V
+@pytest.mark.parametrize("efq", [False, True])
+def test_equal_scores_give_the_mean_of_v(mx, efq):
+    # q = 0: every probability is exp(0) = 1 (EFQ: code 6 under 2^-2, also
+    # 1), o = the plain mean of decoded V
     rng = np.random.default_rng(3)
     heads, lq, lk = 2, 40, 160
     q = bf16(np.zeros((heads, lq, D)))
     k = bf16(rng.standard_normal((heads, lk, D)))
     vc, vs = v_input(rng, heads, lk, oracle.FP6_E2M3)
-    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP6_E2M3, q, k, vc, vs, 0.125, torch.float32)
+    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP6_E2M3, q, k, vc, vs, 0.125, torch.float32, efq=efq)
     vt = oracle.dequantize(oracle.FP6_E2M3, vc, vs, None, heads * D, lk, oracle.FP32)
     want = vt.reshape(heads, D, lk).astype(np.float64).mean(-1)
     assert np.allclose(o, np.broadcast_to(want[:, None, :], o.shape), rtol=1e-6, atol=1e-7)
     assert np.all(rs == lk) and np.all(rm == 0.0)
 
 
-def test_one_dominant_key_gives_its_v_row(mx):
+@pytest.mark.parametrize("efq", [False, True])
+def test_one_dominant_key_gives_its_v_row(mx, efq):
     rng = np.random.default_rng(4)
     heads, lq, lk = 1, 64, 256
     qf = np.zeros((heads, lq, D), np.float32)
@@ -183,22 +193,24 @@ def test_one_dominant_key_gives_its_v_row(mx):
     kf[0, 200, 0] = 120.0
     vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
     o, rm, rs, pc, ps = run_gpu(mx, oracle.FP8_E4M3, bf16(qf), bf16(kf), vc, vs, 1.0,
-                                torch.float32)
+                                torch.float32, efq=efq)
     vt = oracle.dequantize(oracle.FP8_E4M3, vc, vs, None, heads * D, lk, oracle.FP32)
     assert np.array_equal(o[0], np.broadcast_to(vt.reshape(D, lk)[:, 200], (lq, D)))
     assert np.all(rm == 120.0) and np.all(rs == 1.0)
 
 
-def test_nan_score_poisons_its_row_only(mx):
+@pytest.mark.parametrize("efq", [False, True])
+def test_nan_score_poisons_its_row_only(mx, efq):
     rng = np.random.default_rng(5)
     heads, lq, lk = 1, 64, 128
     qf = rng.standard_normal((heads, lq, D)).astype(np.float32)
     qf[0, 9, 17] = np.nan
     q, k = bf16(qf), bf16(rng.standard_normal((heads, lk, D)))
     vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
-    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP8_E4M3, q, k, vc, vs, 0.1, torch.bfloat16)
+    o, rm, rs, pc, ps = run_gpu(mx, oracle.FP8_E4M3, q, k, vc, vs, 0.1, torch.bfloat16, efq=efq)
     _, _, _, pc_ref, ps_ref = oracle.attention_fwd(oracle.FP8_E4M3, q, k, vc, vs, 0.1, 64,
-                                                   oracle.BF16)
+                                                   oracle.BF16, efq=efq)
+    assert np.array_equal(pc, pc_ref) and np.array_equal(ps, ps_ref)
     assert np.all(o[0, 9] == 0x7FC0)  # canonical bf16 NaN
     assert np.all(ps[0, 9] == 0xFF) and np.all(ps_ref[0, 9] == 0xFF)
     others = np.delete(np.arange(lq), 9)
