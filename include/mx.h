@@ -192,9 +192,9 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void *q,
 
 /* The same attention forward with EFQ's exp-free probability blocks ("EFQ-
  * Softmax" explainer, the paragraph that starts "Concretely" and the stage
- * table: no exp(); an exponent-only scale from the block's local maximum
- * normalizes the shifted scores and one affine rule maps them to
- * nonnegative E2M1 codes).  The page prints no constants; this library's
+ * table: no exp(); a power-of-two scale taken from the largest value in the
+ * block normalizes the shifted scores, and a single affine rule turns them
+ * into E2M1 codes without a sign).  The page prints no constants; this library's
  * reading, identical in the CPU reference:
  *   u = fp32((t - m_new) * log2 e) for the block's 32 keys,
  *   byte = clamp(floor(max u) - 2 + 127, 0, 254) (the MX rule on 2^max u),

@@ -531,8 +531,8 @@ static double bf16_value(uint16_t b) {
 /* ------------------------------------------------------------------ */
 /* EFQ's exp-free probability block ([EFQ] article, the paragraph that  */
 /* starts "Concretely", and the stage table): no exp(); an exponent-     */
-/* only scale chosen from the block's local maximum normalizes the      */
-/* shifted scores, and one affine rule maps them to nonnegative E2M1    */
+/* only scale taken from the largest value in the block normalizes the */
+/* shifted scores, and a single affine rule turns them into unsigned     */
 /* codes.  The pages give no constants, so the rule below is a reading  */
 /* (PARITY UNPINNED by the pages; only its stated properties are       */
 /* tested):                                                             */

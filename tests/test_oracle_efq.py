@@ -1,7 +1,7 @@
 """EFQ's exp-free probability blocks in the oracle (CPU only).
 
 The EFQ explainer says what the rule does (an exponent-only block scale
-from the block's local maximum, then one affine map from shifted scores to
+taken from the largest value in the block, then one affine map from shifted scores to
 nonnegative E2M1 codes, no exp) but prints no constants, so the oracle
 implements a stated reading: u = fp32(d log2 e), byte = the MX rule on 2^U
 (U = max u), w = u - (byte - 127), code = trunc(clamp(2w + 2.5, 0, 7.5)).
