@@ -56,7 +56,8 @@ typedef __attribute__((address_space(1))) const void glob_void_t;
 
 constexpr int kD = 128;              // head dimension
 constexpr int kTile = 64;            // keys per online-softmax step
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;           // waves per workgroup (a multiple of 4)
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // queries per workgroup
 constexpr int kKBytes = kTile * 2 * kD;  // one K tile in LDS: 64 rows of 256 B
 
@@ -116,8 +117,8 @@ __device__ __forceinline__ void lds_load12(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)l, 12, 0, 0);
 }
 
-// Direct loads of one key tile into one LDS buffer.  Each wave issues 4 K
-// and up to 2 V instructions; every lane's address is a fixed per-lane
+// Direct loads of one key tile into one LDS buffer.  Each wave issues
+// 16 / kWaves K and up to 8 / kWaves V instructions; every lane's address is a fixed per-lane
 // offset plus a per-tile base that is the same for the whole wave, so the
 // per-tile cost is scalar arithmetic.  K rows past lk and a missing second
 // V block (a last tile of 32 keys) re-read valid data; the kernel masks
@@ -127,7 +128,7 @@ struct TileLoader {
   using L = VTile<VF>;
   const uint8_t* kh;  // this head's K
   const uint8_t* vh;  // this head's V^T codes
-  int64_t vrows64;    // bytes of 64 V^T rows
+  int64_t vstep;      // bytes of the V^T rows one round of instructions covers
   uint32_t koff;      // lane's K byte offset inside a tile (instruction 0)
   uint32_t voff;      // lane's V byte offset (instruction 0, tile 0)
   uint32_t vhalf;     // bytes back to the first block when the lane's chunk is in the second
@@ -140,13 +141,14 @@ struct TileLoader {
     wave = wave_;
     kh = reinterpret_cast<const uint8_t*>(k) + (int64_t)bh * lk * (2 * kD);
     vh = vc + (int64_t)bh * kD * nbk * L::BPB;
-    vrows64 = (int64_t)64 * nbk * L::BPB;
-    // K chunk c = 64 (4n + wave) + lane: row 16n + 4 wave + lane / 16, slot
-    // lane % 16, logical chunk slot ^ (row % 16) (n does not change it)
+    vstep = (int64_t)(kThreads / L::CPR) * nbk * L::BPB;
+    // K chunk c = 64 (kWaves n + wave) + lane: row 4 kWaves n + 4 wave +
+    // lane / 16, slot lane % 16, logical chunk slot ^ (row % 16) (n does
+    // not change it: 4 kWaves is a multiple of 16)
     const int r0 = 4 * wave + (lane >> 4);
     koff = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ (r0 & 15)));
-    // V chunk c = 64 (4n + wave) + lane: row c / CPR, slot c % CPR (n adds
-    // 64 rows and does not change the swizzle)
+    // V chunk c = 64 (kWaves n + wave) + lane: row c / CPR, slot c % CPR (n
+    // adds kThreads / CPR rows and does not change the swizzle)
     const int c0 = wave * 64 + lane;
     const int d0 = c0 / L::CPR;
     const int ch = (c0 - d0 * L::CPR) ^ L::swz(d0);
@@ -158,21 +160,22 @@ struct TileLoader {
     const int key0 = jt * kTile, kb0 = 2 * jt;
     const bool two = kb0 + 1 < nbk;
     const uint8_t* kt = kh + (int64_t)key0 * (2 * kD);
+    constexpr int kRowsPerRound = 4 * kWaves;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      // rows 16n.. of a 32-key last tile do not exist for n >= 2: re-read
-      // rows 16n - 32..
-      const uint8_t* base = kt + (int64_t)(n * 16 - ((!two && n >= 2) ? 32 : 0)) * (2 * kD);
-      lds_load16(base + koff, ksb + (4 * n + wave) * 64 * 16);
+    for (int n = 0; n < kTile / kRowsPerRound; ++n) {
+      // rows 32.. of a 32-key last tile do not exist: re-read rows 0..
+      const int r = n * kRowsPerRound;
+      const uint8_t* base = kt + (int64_t)(r - ((!two && r >= 32) ? 32 : 0)) * (2 * kD);
+      lds_load16(base + koff, ksb + (kWaves * n + wave) * 64 * 16);
     }
     const uint32_t vo = two ? voff : voff - vhalf;
     const uint8_t* vt = vh + (int64_t)kb0 * L::BPB;
     constexpr int nchunks = kD * L::CPR;
 #pragma unroll
-    for (int n = 0; n < (nchunks + 255) / 256; ++n) {
-      if ((4 * n + wave) * 64 < nchunks) {
-        const uint8_t* src = vt + n * vrows64 + vo;
-        uint8_t* dst = vsb + (4 * n + wave) * 64 * 16;
+    for (int n = 0; n < (nchunks + kThreads - 1) / kThreads; ++n) {
+      if ((kWaves * n + wave) * 64 < nchunks) {
+        const uint8_t* src = vt + n * vstep + vo;
+        uint8_t* dst = vsb + (kWaves * n + wave) * 64 * 16;
         if constexpr (L::CH == 16) lds_load16(src, dst);
         else lds_load12(src, dst);
       }
@@ -181,7 +184,7 @@ struct TileLoader {
 };
 
 template <int VF, bool OUT_BF16, bool EFQ>
-__global__ __launch_bounds__(256, 2) void attention_fwd_mx(
+__global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs, int lq, int lk,
     float scale, int qtiles, void* __restrict__ o, float* __restrict__ row_max,
@@ -462,7 +465,7 @@ hipError_t launch_vf(bool out_bf16, const void* q, const void* k, const void* vc
                      const uint8_t* vs, int heads, int lq, int lk, float scale, void* o,
                      float* rm, float* rs, uint8_t* pc, uint8_t* ps, hipStream_t st) {
   const int qtiles = (lq + kRows - 1) / kRows;
-  const dim3 grid((unsigned)(heads * qtiles)), block(256);
+  const dim3 grid((unsigned)(heads * qtiles)), block(kThreads);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint8_t* v8 = static_cast<const uint8_t*>(vc);
