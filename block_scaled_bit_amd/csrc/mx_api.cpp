@@ -40,6 +40,8 @@ mxk::ExmyParams exmy_params(int f) {
     p.maxf = ldexpf(1.0f, m) - 1.0f;
   }
   p.bias = 1 - p.emin;
+  p.dec_bits = (uint32_t)(127 - p.bias) << 23;
+  p.dec_sub = -ldexpf(1.0f, 1 - p.bias);
   return p;
 }
 bool dtype_ok(int d) { return d == MX_BF16 || d == MX_FP32; }

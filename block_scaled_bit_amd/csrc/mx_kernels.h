@@ -12,13 +12,17 @@ namespace mxk {
 // Generic eXmY format parameters (prepared on the host): m mantissa bits;
 // emin = exponent of the smallest normal (m for integer formats); emax =
 // floor(log2 of the largest magnitude); bias = 1 - emin; maxf = the largest
-// magnitude.
+// magnitude; dec_bits, dec_sub as below.
 struct ExmyParams {
   int m;
   int emin;
   int emax;
   int bias;
   float maxf;
+  // decoding constants: the fp32 exponent-field offset (127 - bias) << 23
+  // and -2^(1 - bias)
+  uint32_t dec_bits;
+  float dec_sub;
 };
 
 hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,

@@ -375,29 +375,27 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
 // a tie 1.5 * 2^k would pick the larger value, so an odd code there is
 // moved down by one.
 // ---------------------------------------------------------------------------
+template <bool M0>
 __device__ __forceinline__ uint32_t exmy_round(float a, const ExmyParams& p) {
+  // a >= 0, at most the largest magnitude.  The grid step at a is 2^(et -
+  // 127 - m) with et = max(a's biased exponent, 127 + emin); adding C =
+  // 2^(et - 127 + 23 - m) leaves a rounded to that step (nearest, ties to
+  // even) in the low mantissa bits of the sum, and the binade's first code
+  // is (et - 127 - emin) << m.
   const uint32_t ab = __float_as_uint(a);
-  const int ea = (int)(ab >> 23);
-  const int et = ea > 127 + p.emin ? ea : 127 + p.emin;
-  const float C = __uint_as_float((uint32_t)(et + 23 - p.m) << 23);
-  const float sum = a + C;
-  uint32_t mag = (__float_as_uint(sum) - __float_as_uint(C)) + ((uint32_t)(et - 127 - p.emin) << p.m);
-  if (p.m == 0 && ea >= 127 + p.emin && (ab & 0x7FFFFFu) == 0x400000u && (mag & 1u)) mag -= 1u;
+  const uint32_t emin_b = (uint32_t)(127 + p.emin);
+  const uint32_t et = max(ab >> 23, emin_b);
+  const float C = __uint_as_float((et + (uint32_t)(23 - p.m)) << 23);
+  uint32_t mag = __float_as_uint(a + C) - __float_as_uint(C) + ((et - emin_b) << p.m);
+  if constexpr (M0) {
+    // exponent-only formats: a tie between two powers of two goes to the
+    // even exponent field, which the adder does not know about
+    if ((ab >> 23) >= emin_b && (ab & 0x7FFFFFu) == 0x400000u && (mag & 1u)) mag -= 1u;
+  }
   return mag;
 }
 
-__device__ __forceinline__ float exmy_decode(uint32_t mag, int scale_exp, const ExmyParams& p) {
-  const uint32_t e = mag >> p.m;
-  const uint32_t mant = mag & ((1u << p.m) - 1u);
-  const uint32_t sig = e ? (mant | (1u << p.m)) : mant;
-  const int ex = (int)(e ? e : 1u) - p.bias - p.m;  // bias = 1 - emin
-  return __builtin_ldexpf((float)sig, ex + scale_exp);
-}
-
-__device__ __forceinline__ uint32_t exmy_block_byte(const uint32_t (&v)[32], const ExmyParams& p) {
-  uint32_t amax = 0u;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) amax = max(amax, v[k] & 0x7FFFFFFFu);
+__device__ __forceinline__ uint32_t exmy_byte_from_amax(uint32_t amax, const ExmyParams& p) {
   if (amax >= 0x7F800000u) return 0xFFu;
   if (amax == 0u) return 0u;
   const int field = (int)(amax >> 23);
@@ -407,35 +405,66 @@ __device__ __forceinline__ uint32_t exmy_block_byte(const uint32_t (&v)[32], con
   return (uint32_t)(b > 254 ? 254 : b);
 }
 
-template <int W>
+// The value of magnitude code mag times 2^scale_exp (exact before the
+// final rounding of ldexp).  Normal codes: the fp32 bit pattern is mag
+// shifted so its exponent field lands on fp32's, plus the bias difference.
+// Subnormal codes (exponent field 0, and every code of an integer format):
+// the same pattern reads (1 + mant / 2^m) 2^-bias, and 2x - 2^(1 - bias)
+// is mant / 2^m 2^(1 - bias).
+__device__ __forceinline__ float exmy_decode(uint32_t mag, int scale_exp, const ExmyParams& p) {
+  const float f = __uint_as_float((mag << (23 - p.m)) + p.dec_bits);
+  const float sub = __builtin_fmaf(f, 2.0f, p.dec_sub);
+  return __builtin_ldexpf(mag < (1u << p.m) ? sub : f, scale_exp);
+}
+
+__device__ __forceinline__ uint32_t exmy_block_byte(const uint32_t (&v)[32], const ExmyParams& p) {
+  return exmy_byte_from_amax(amax_f32x32(v), p);
+}
+
+template <int W, bool M0>
 __device__ __forceinline__ void exmy_codes(const uint32_t (&v)[32], uint32_t byte,
                                            const ExmyParams& p, uint32_t (&c)[32]) {
+  // a poisoned block (byte 0xFF) gives arbitrary codes here; the callers
+  // zero them
   const int neg_exp = 127 - (int)byte;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const float a = fminf(__builtin_ldexpf(__uint_as_float(v[k] & 0x7FFFFFFFu), neg_exp), p.maxf);
-    c[k] = (byte == 0xFFu) ? 0u : (exmy_round(a, p) | ((v[k] >> 31) << (W - 1)));
+    const float a =
+        fminf(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(v[k])), neg_exp), p.maxf);
+    c[k] = exmy_round<M0>(a, p) | ((v[k] >> 31) << (W - 1));
   }
 }
 
-template <int W, bool BF16>
+template <int W, bool BF16, bool M0>
 __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x, int64_t nb,
                                                      uint32_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales, ExmyParams p) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     uint32_t v[32], c[32], o[W];
-    load_values<BF16>(x, b, v);
-    const uint32_t byte = exmy_block_byte(v, p);
-    exmy_codes<W>(v, byte, p, c);
+    uint32_t byte;
+    if constexpr (BF16) {
+      uint32_t d[16];
+      load_bf16_block(x, b, d);
+      byte = exmy_byte_from_amax(amax_bf16x32(d), p);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[2 * k] = d[k] << 16;
+        v[2 * k + 1] = d[k] & 0xFFFF0000u;
+      }
+    } else {
+      load_f32_block(x, b, v);
+      byte = exmy_byte_from_amax(amax_f32x32(v), p);
+    }
+    exmy_codes<W, M0>(v, byte, p, c);
     pack32<W>(c, o);
 #pragma unroll
-    for (int j = 0; j < W; ++j) codes[b * W + j] = o[j];  // 4W bytes per block
+    for (int j = 0; j < W; ++j) codes[b * W + j] = byte == 0xFFu ? 0u : o[j];  // 4W bytes
     scales[b] = (uint8_t)byte;
   }
 }
 
-template <int W, bool BF16>
+template <int W, bool BF16, bool M0>
 __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t nb, void* y,
                                                           ExmyParams p) {
   constexpr int NCH = BF16 ? 4 : 8;
@@ -447,7 +476,7 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
     uint32_t v[32] = {}, c[32], out[32];
     if (b < nb) load_values<BF16>(x, b, v);
     const uint32_t byte = exmy_block_byte(v, p);
-    exmy_codes<W>(v, byte, p, c);
+    exmy_codes<W, M0>(v, byte, p, c);
     const int sexp = (int)byte - 127;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
@@ -493,14 +522,27 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
     for (int k = 0; k < 32; ++k) {
       const uint32_t code = unpack1<W>(o, k);
       const float val = exmy_decode(code & ((1u << (W - 1)) - 1u), sexp, p);
-      out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(val) | ((code >> (W - 1)) << 31));
+      out[k] = __float_as_uint(val) | ((code >> (W - 1)) << 31);
+    }
+    if (byte == 0xFFu) {  // rare: a poisoned block
+#pragma unroll
+      for (int k = 0; k < 32; ++k) out[k] = kNaN32;
     }
     if constexpr (BF16) {
+      // every eXmY value has at most 8 significant bits, so it is a bf16
+      // value whenever it is an fp32 normal (or zero, inf, NaN): the top
+      // half of the bit pattern, no rounding.  Only blocks whose smallest
+      // nonzero magnitude is an fp32 subnormal take the rounding path.
       uint32_t d[16];
+      if (p.emin - p.m + sexp >= -126 || byte == 0xFFu) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        d[k] = f32_to_bf16_rne(__uint_as_float(out[2 * k])) |
-               (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
+        for (int k = 0; k < 16; ++k) d[k] = __builtin_amdgcn_perm(out[2 * k + 1], out[2 * k], 0x07060302u);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          d[k] = f32_to_bf16_rne(__uint_as_float(out[2 * k])) |
+                 (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
+      }
       store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
       store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
@@ -735,18 +777,38 @@ hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const 
                        hipStream_t st) {
   const dim3 block(256);
   const dim3 grid = (op == 0) ? grid_for(nb, 256) : grid_for(nb, 4 * kTile);
-  MXK_SWITCH_WIDTH(width, {
-    if (op == 0) {
-      if (bf16) hipLaunchKernelGGL((quantize_exmy<WW, true>), grid, block, 0, st, in, nb, (uint32_t*)out, scales_out, p);
-      else hipLaunchKernelGGL((quantize_exmy<WW, false>), grid, block, 0, st, in, nb, (uint32_t*)out, scales_out, p);
-    } else if (op == 1) {
-      if (bf16) hipLaunchKernelGGL((dequantize_exmy<WW, true>), grid, block, 0, st, (const uint32_t*)in, scales_in, nb, out, p);
-      else hipLaunchKernelGGL((dequantize_exmy<WW, false>), grid, block, 0, st, (const uint32_t*)in, scales_in, nb, out, p);
-    } else {
-      if (bf16) hipLaunchKernelGGL((fake_quantize_exmy<WW, true>), grid, block, 0, st, in, nb, out, p);
-      else hipLaunchKernelGGL((fake_quantize_exmy<WW, false>), grid, block, 0, st, in, nb, out, p);
-    }
-  });
+  // exponent-only formats (m = 0) need the even-exponent tie rule
+#define MXK_EXMY_LAUNCH(M0)                                                                     \
+  MXK_SWITCH_WIDTH(width, {                                                                     \
+    if (op == 0) {                                                                              \
+      if (bf16)                                                                                 \
+        hipLaunchKernelGGL((quantize_exmy<WW, true, M0>), grid, block, 0, st, in, nb,           \
+                           (uint32_t*)out, scales_out, p);                                      \
+      else                                                                                      \
+        hipLaunchKernelGGL((quantize_exmy<WW, false, M0>), grid, block, 0, st, in, nb,          \
+                           (uint32_t*)out, scales_out, p);                                      \
+    } else if (op == 1) {                                                                       \
+      if (bf16)                                                                                 \
+        hipLaunchKernelGGL((dequantize_exmy<WW, true>), grid, block, 0, st,                     \
+                           (const uint32_t*)in, scales_in, nb, out, p);                         \
+      else                                                                                      \
+        hipLaunchKernelGGL((dequantize_exmy<WW, false>), grid, block, 0, st,                    \
+                           (const uint32_t*)in, scales_in, nb, out, p);                         \
+    } else {                                                                                    \
+      if (bf16)                                                                                 \
+        hipLaunchKernelGGL((fake_quantize_exmy<WW, true, M0>), grid, block, 0, st, in, nb, out, \
+                           p);                                                                  \
+      else                                                                                      \
+        hipLaunchKernelGGL((fake_quantize_exmy<WW, false, M0>), grid, block, 0, st, in, nb,     \
+                           out, p);                                                             \
+    }                                                                                           \
+  })
+  if (p.m == 0) {
+    MXK_EXMY_LAUNCH(true);
+  } else {
+    MXK_EXMY_LAUNCH(false);
+  }
+#undef MXK_EXMY_LAUNCH
   return hipGetLastError();
 }
 
