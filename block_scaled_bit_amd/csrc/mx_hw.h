@@ -138,6 +138,54 @@ __device__ __forceinline__ void encode_f32(const uint32_t (&d)[32], float sc, ui
 }
 
 // ---------------------------------------------------------------------------
+// Encode one half block (values 16h..16h+15 of a block, as fp32 patterns)
+// under sc into the W/2 code dwords that hold exactly those values (the
+// packed layouts above put the first 16 codes in the first W/2 dwords).
+// FP6: the 32-wide instruction with its last 16 inputs zero, whose codes
+// land in the dwords that are dropped.
+// ---------------------------------------------------------------------------
+template <int F>
+__device__ __forceinline__ void encode_f32_half(const uint32_t (&d)[16], float sc,
+                                                uint32_t (&o)[Fmt<F>::W / 2]) {
+  if constexpr (F == F_E2M3 || F == F_E3M2) {
+    f32x16_t a, b;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      a[k] = k < 8 ? __uint_as_float(d[2 * k]) : 0.0f;
+      b[k] = k < 8 ? __uint_as_float(d[2 * k + 1]) : 0.0f;
+    }
+    u32x6_t r;
+    if constexpr (F == F_E2M3) r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, sc);
+    else r = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, sc);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) o[k] = r[k];
+  } else if constexpr (F == F_E2M1) {
+#define MXK_FP4_F32(w, j, s) \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(d[8 * (j) + 2 * (s)]), \
+                                           __uint_as_float(d[8 * (j) + 2 * (s) + 1]), sc, s)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t w = 0;
+      w = MXK_FP4_F32(w, j, 0);
+      w = MXK_FP4_F32(w, j, 1);
+      w = MXK_FP4_F32(w, j, 2);
+      w = MXK_FP4_F32(w, j, 3);
+      o[j] = w;
+    }
+#undef MXK_FP4_F32
+  } else {
+    static_assert(F == F_E4M3, "hardware encode covers the MX formats");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s16x2_t w = {0, 0};
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, __uint_as_float(d[4 * j]), __uint_as_float(d[4 * j + 1]), sc, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, __uint_as_float(d[4 * j + 2]), __uint_as_float(d[4 * j + 3]), sc, true);
+      o[j] = e4m3_saturate4(__builtin_bit_cast(uint32_t, w));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode one block of W code dwords under sc: 32 bf16 as 16 dwords, or 32
 // fp32 bit patterns.  NaN results (E4M3 NaN codes) are left as the
 // instruction produces them; the caller canonicalizes.

@@ -552,84 +552,145 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
 
 // ---------------------------------------------------------------------------
 // Exp-then-quantize probabilities: one wavefront per row (exp_ref_nonpos is
-// the fixed fp32 exp sequence, in mx_exp.h).
+// the fixed fp32 exp sequence, in mx_exp.h).  Two lanes share a block: lanes
+// 2i and 2i+1 hold its two 16-value halves, so a lane reads 64 contiguous
+// bytes per half block (fp32 rows stream ~25 % faster that way on this part
+// than with a whole 128-byte block per lane), and the pair exchanges its
+// half maxima with one DPP move before deriving the block's scale.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Largest of the wave's 64 values (NaN-free inputs), in every lane: DPP
+// within each row of 16 lanes (swap pairs, swap pair-of-pairs, mirror the
+// half row, mirror the row), then the four row results read as scalars.
 __device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
+  m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_f32<0x140>(m));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ __forceinline__ int wave_or(int f) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) f |= __shfl_xor(f, off, 64);
-  return f;
+// max of v over lanes 2i and 2i+1 (DPP quad_perm [1,0,3,2] swaps the pair)
+__device__ __forceinline__ uint32_t pair_max(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
 }
 
-// Probabilities of one block of shifted scores, quantized; `kind` is the
-// row's case: 0 finite row max, 1 row max +inf (then s - m is -inf, giving
-// P = 0, except NaN where s is +inf itself).
+__device__ __forceinline__ void load_f32_half(const float* row, int64_t h, uint32_t (&d)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(row) + 4 * h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = p[i];
+    d[4 * i] = q.x; d[4 * i + 1] = q.y; d[4 * i + 2] = q.z; d[4 * i + 3] = q.w;
+  }
+}
+
+// Half block hg (global index) of packed codes: W2 dwords at hg * 4 * W2.
+template <int W2>
+__device__ __forceinline__ void store_half(void* codes, int64_t hg, const uint32_t (&o)[W2]) {
+  if constexpr (W2 == 2) {
+    reinterpret_cast<uint2*>(codes)[hg] = make_uint2(o[0], o[1]);
+  } else if constexpr (W2 == 4) {
+    reinterpret_cast<uint4*>(codes)[hg] = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    static_assert(W2 == 3, "FP6 half blocks are 3 dwords");
+    uint32_t* p = reinterpret_cast<uint32_t*>(codes) + 3 * hg;
+    p[0] = o[0]; p[1] = o[1]; p[2] = o[2];
+  }
+}
+
+// Probabilities of one half block of shifted scores and its codes under the
+// block's scale; `kind` is the row's case: 0 finite row max, 1 row max +inf
+// (then s - m is -inf, giving P = 0, except NaN where s is +inf itself).
+// Every lane of the wave calls it together (the pair exchange).
 template <int F>
-__device__ __forceinline__ void probs_block(const uint32_t (&sv)[32], float m, int kind,
-                                           uint32_t (&o)[Fmt<F>::W], uint32_t& byte) {
-  uint32_t v[32];
+__device__ __forceinline__ void probs_half(const uint32_t (&sv)[16], float m, int kind,
+                                           uint32_t (&o)[Fmt<F>::W / 2], uint32_t& byte) {
+  uint32_t v[16];
   if (kind == 0) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] = __float_as_uint(exp_ref_nonpos(__uint_as_float(sv[k]) - m));
+    for (int k = 0; k < 16; ++k) v[k] = __float_as_uint(exp_ref_nonpos(__uint_as_float(sv[k]) - m));
   } else {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] = (sv[k] == 0x7F800000u) ? 0x7FC00000u : 0u;
+    for (int k = 0; k < 16; ++k) v[k] = (sv[k] == 0x7F800000u) ? 0x7FC00000u : 0u;
   }
   uint32_t amax = 0u;  // P >= 0 (or NaN), so the bit patterns order as values
 #pragma unroll
-  for (int k = 0; k < 32; ++k) amax = max(amax, v[k]);
-  byte = scale_byte_from_amax<F>(amax);
-  encode_f32<F>(v, scale_operand(byte), o);
+  for (int k = 0; k < 16; ++k) amax = max(amax, v[k]);
+  byte = scale_byte_from_amax<F>(pair_max(amax));
+  encode_f32_half<F>(v, scale_operand(byte), o);
   if (byte == 0xFFu) {
 #pragma unroll
-    for (int k = 0; k < Fmt<F>::W; ++k) o[k] = 0u;
+    for (int k = 0; k < Fmt<F>::W / 2; ++k) o[k] = 0u;
   }
 }
 
-// One wavefront per row.  RB > 0: lane l keeps blocks l, l+64, ... (at most
-// RB of them, enough for the whole row) in registers, so the row is read
-// once.  RB == 0: rows of any length; the second pass reads the row again.
-template <int F, int RB>
-__global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __restrict__ s,
+// One wavefront per row of nh = 2 * cols / 32 half blocks (the launcher
+// splits row counts beyond one grid).  HB > 0: lane l
+// keeps half blocks l, l+64, ... (at most HB of them, enough for the whole
+// row) in registers, so the row is read once.  HB == 0: rows of any length;
+// the second pass reads the row again.  Half blocks past the row's end read
+// nothing (their values are -inf, so P = 0) and store nothing; the two
+// halves of a block are always on the same side of the end.  FULL: nh is
+// exactly 64 * HB, so no lane needs that test (exec-masked loads and stores
+// cost ~4 % of the kernel's time on 4096-column rows).
+// Occupancy: five waves per SIMD where the row fits (the kernel streams
+// reads and writes at once, and four waves leave the memory system short of
+// requests), two for rows of 512 half blocks (128 registers of row data).
+template <int F, int HB, bool FULL>
+__global__ __launch_bounds__(256, HB == 8 ? 2 : 5) void softmax_quantize_rows(const float* __restrict__ s,
                                                              int64_t rows, int64_t cols,
                                                              void* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
-  constexpr int W = Fmt<F>::W;
+  constexpr int W2 = Fmt<F>::W / 2;
+  constexpr uint32_t kNegInf = 0xFF800000u;
   const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t nbr = cols >> 5;
-  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); row < rows;
-       row += waves) {
+  const int64_t nbr = cols >> 5, nh = 2 * nbr;
+  {
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    // per-row bases are the same for the whole wave; lane offsets are small
     const float* srow = s + row * cols;
-    uint32_t keep[RB > 0 ? RB : 1][32];
+    uint8_t* crow = reinterpret_cast<uint8_t*>(codes) + row * nh * (4 * W2);
+    uint8_t* srow_scales = scales + row * nbr;
+    uint32_t keep[HB > 0 ? HB : 1][16];
     // pass 1: exact row maximum; a NaN anywhere poisons the whole row
     float m = -__builtin_inff();
     bool nan_seen = false;
-    if constexpr (RB > 0) {
+    if constexpr (HB > 0) {
+      // every load of the row is issued before the first use, so the whole
+      // row is in flight at once
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int64_t j = lane + 64 * i;
-        if (j < nbr) {
-          load_f32_block(srow, j, keep[i]);
+      for (int i = 0; i < HB; ++i) {
+        if (FULL || lane + 64 * i < nh) {
+          load_f32_half(srow, lane + 64 * i, keep[i]);
+        } else {
 #pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const float x = __uint_as_float(keep[i][k]);
-            nan_seen |= (x != x);
-            m = fmaxf(m, x);
-          }
+          for (int k = 0; k < 16; ++k) keep[i][k] = kNegInf;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < HB; ++i) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float x = __uint_as_float(keep[i][k]);
+          nan_seen |= (x != x);
+          m = fmaxf(m, x);
         }
       }
     } else {
-      for (int64_t j = lane; j < nbr; j += 64) {
-        uint32_t v[32];
-        load_f32_block(srow, j, v);
+      for (int64_t h = lane; h < nh; h += 64) {
+        uint32_t v[16];
+        load_f32_half(srow, h, v);
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
+        for (int k = 0; k < 16; ++k) {
           const float x = __uint_as_float(v[k]);
           nan_seen |= (x != x);
           m = fmaxf(m, x);
@@ -639,40 +700,49 @@ __global__ __launch_bounds__(256) void softmax_quantize_rows(const float* __rest
     m = wave_max(m);
     // a NaN in the row, or a row of only -inf (then s - m = -inf - -inf is
     // NaN everywhere), poisons every block of the row
-    const bool row_nan = wave_or(nan_seen ? 1 : 0) != 0 || m == -__builtin_inff();
+    const bool row_nan = __ballot(nan_seen) != 0 || m == -__builtin_inff();
     const int kind = (m == __builtin_inff()) ? 1 : 0;
-    // pass 2: P = exp(s - m) per block, then quantize the block
-    if constexpr (RB > 0) {
+    // pass 2: P = exp(s - m) per half block, then the block's scale and codes
+    if constexpr (HB > 0) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int64_t j = lane + 64 * i;
-        if (j < nbr) {
-          uint32_t o[W];
-          uint32_t byte = 0xFFu;
-          if (row_nan) {
-#pragma unroll
-            for (int k = 0; k < W; ++k) o[k] = 0u;
-          } else {
-            probs_block<F>(keep[i], m, kind, o, byte);
-          }
-          store_codes<W>(codes, row * nbr + j, o);
-          scales[row * nbr + j] = (uint8_t)byte;
-        }
-      }
-    } else {
-      for (int64_t j = lane; j < nbr; j += 64) {
-        uint32_t o[W];
+      for (int i = 0; i < HB; ++i) {
+        const int h = lane + 64 * i;
+        uint32_t o[W2];
         uint32_t byte = 0xFFu;
         if (row_nan) {
 #pragma unroll
-          for (int k = 0; k < W; ++k) o[k] = 0u;
+          for (int k = 0; k < W2; ++k) o[k] = 0u;
         } else {
-          uint32_t sv[32];
-          load_f32_block(srow, j, sv);
-          probs_block<F>(sv, m, kind, o, byte);
+          probs_half<F>(keep[i], m, kind, o, byte);
         }
-        store_codes<W>(codes, row * nbr + j, o);
-        scales[row * nbr + j] = (uint8_t)byte;
+        if (FULL || h < nh) {
+          store_half<W2>(crow, h, o);
+          if (!(lane & 1)) srow_scales[h >> 1] = (uint8_t)byte;
+        }
+      }
+    } else {
+      // the loop bound is the same for every lane, so whole pairs take part
+      for (int64_t h0 = 0; h0 < nh; h0 += 64) {
+        const int64_t h = h0 + lane;
+        uint32_t o[W2];
+        uint32_t byte = 0xFFu;
+        if (row_nan) {
+#pragma unroll
+          for (int k = 0; k < W2; ++k) o[k] = 0u;
+        } else {
+          uint32_t sv[16];
+          if (h < nh) {
+            load_f32_half(srow, h, sv);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sv[k] = kNegInf;
+          }
+          probs_half<F>(sv, m, kind, o, byte);
+        }
+        if (h < nh) {
+          store_half<W2>(crow, h, o);
+          if (!(lane & 1)) srow_scales[h >> 1] = (uint8_t)byte;
+        }
       }
     }
   }
@@ -742,22 +812,51 @@ hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, v
   return hipGetLastError();
 }
 
+// Rows that fill HB half blocks per lane exactly take the variant without
+// end-of-row tests.
+template <int F, int HB>
+static void launch_rows(dim3 grid, hipStream_t st, const float* s, int64_t rows, int64_t cols,
+                        void* codes, uint8_t* scales) {
+  if constexpr (HB > 0) {
+    if (2 * (cols / 32) == 64 * HB) {
+      hipLaunchKernelGGL((softmax_quantize_rows<F, HB, true>), grid, dim3(256), 0, st, s, rows,
+                         cols, codes, scales);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((softmax_quantize_rows<F, HB, false>), grid, dim3(256), 0, st, s, rows, cols,
+                     codes, scales);
+}
+
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,
                                    void* codes, uint8_t* scales, hipStream_t st) {
-  const dim3 grid = grid_for(rows, 4), block(256);
-  const int64_t nbr = cols / 32;
-  // rows of up to 64, 128 or 256 blocks stay in registers (read once)
-  MXK_SWITCH_MX(fmt, {
-    if (nbr <= 64)
-      hipLaunchKernelGGL((softmax_quantize_rows<FF, 1>), grid, block, 0, st, s, rows, cols, codes, scales);
-    else if (nbr <= 128)
-      hipLaunchKernelGGL((softmax_quantize_rows<FF, 2>), grid, block, 0, st, s, rows, cols, codes, scales);
-    else if (nbr <= 256)
-      hipLaunchKernelGGL((softmax_quantize_rows<FF, 4>), grid, block, 0, st, s, rows, cols, codes, scales);
-    else
-      hipLaunchKernelGGL((softmax_quantize_rows<FF, 0>), grid, block, 0, st, s, rows, cols, codes, scales);
-  });
-  return hipGetLastError();
+  const int64_t nbr = cols / 32, nh = 2 * nbr;
+  // one wave per row, four per workgroup; a grid holds 2^31 - 1 workgroups
+  const int64_t kRowsPerLaunch = 4 * (int64_t)0x7FFFFFFF;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t n = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const dim3 grid = grid_for(n, 4);
+    const float* sp = s + r0 * cols;
+    uint8_t* sc = scales + r0 * nbr;
+    void* cp = nullptr;
+    // rows of up to 64, 128, 256 or 512 half blocks stay in registers (read once)
+    MXK_SWITCH_MX(fmt, {
+      cp = static_cast<uint8_t*>(codes) + r0 * nbr * (4 * Fmt<FF>::W);
+      if (nh <= 64)
+        (launch_rows<FF, 1>)(grid, st, sp, n, cols, cp, sc);
+      else if (nh <= 128)
+        (launch_rows<FF, 2>)(grid, st, sp, n, cols, cp, sc);
+      else if (nh <= 256)
+        (launch_rows<FF, 4>)(grid, st, sp, n, cols, cp, sc);
+      else if (nh <= 512)
+        (launch_rows<FF, 8>)(grid, st, sp, n, cols, cp, sc);
+      else
+        (launch_rows<FF, 0>)(grid, st, sp, n, cols, cp, sc);
+    });
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 #define MXK_SWITCH_WIDTH(w, BODY)                           \

@@ -144,10 +144,11 @@ def test_fake_quantize_parity_and_in_place(mx, fmt, dtype):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3], ids=lambda f: FMT_NAMES[f])
-@pytest.mark.parametrize("cols", [1024, 4096, 4096 + 96, 8192 + 32])
+@pytest.mark.parametrize("cols", [32, 1024, 2048 - 32, 2048, 4096, 4096 + 96, 8192, 8192 + 32])
 def test_softmax_quantize_parity(mx, fmt, cols):
-    # the column counts cover rows held in registers (up to 64, 128 and 256
-    # blocks per row) and rows streamed twice (longer)
+    # the column counts cover rows held in registers (up to 64, 128, 256 and
+    # 512 half blocks per row, one block per lane pair), exactly filling the
+    # lanes or not, and rows streamed twice (longer); 32 is a row of one block
     s = workloads.attn_scores(rows=37, cols=cols)
     s[3, 11] = np.nan
     s[4, 5] = np.inf
@@ -160,6 +161,29 @@ def test_softmax_quantize_parity(mx, fmt, cols):
     oc, os_ = oracle.softmax_quantize(fmt, s)
     assert_bytes_equal(to_host(scales), os_, "scales")
     assert_bytes_equal(to_host(codes), oc, "codes", BPB[fmt])
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3], ids=lambda f: FMT_NAMES[f])
+@pytest.mark.parametrize("cols", [32 * 33, 4096 + 96, 8192 + 32])
+def test_softmax_quantize_writes_only_its_bytes(mx, fmt, cols):
+    # rows whose last lane pairs hold no block: codes and scales end exactly
+    # at the tensor's end, and every byte in between is written
+    rows = 7
+    s = workloads.attn_scores(rows=rows, cols=cols)
+    nb = rows * cols // 32
+    guard = 4096
+    cbuf = torch.full((guard + nb * BPB[fmt] + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((guard + nb + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    st = mx.mx_softmax_quantize(fmt, 32, to_dev(s), rows, cols, cbuf[guard:guard + nb * BPB[fmt]],
+                                sbuf[guard:guard + nb])
+    assert st == 0
+    torch.cuda.synchronize()
+    c, sc = to_host(cbuf), to_host(sbuf)
+    assert np.all(c[:guard] == 0xA5) and np.all(c[guard + nb * BPB[fmt]:] == 0xA5)
+    assert np.all(sc[:guard] == 0xA5) and np.all(sc[guard + nb:] == 0xA5)
+    oc, os_ = oracle.softmax_quantize(fmt, s)
+    assert_bytes_equal(sc[guard:guard + nb], os_, "scales")
+    assert_bytes_equal(c[guard:guard + nb * BPB[fmt]], oc, "codes", BPB[fmt])
 
 
 def test_softmax_quantize_short_rows(mx):
