@@ -8,6 +8,8 @@
 // writes its packed codes (24/16/32 B) and its scale byte.  No value crosses
 // lanes, so every output byte has exactly one writer and in-place
 // fake-quantization is safe (a lane reads its block before writing it).
+// The exp-then-quantize kernel is the exception: there two lanes share a
+// block (see its section below).
 //
 // Rules: "Online MXFP6" page ("Start a model": packed codes and an E8M0
 // scale per 32 values); "EFQ-Softmax" explainer (exponent-only block scale
