@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "mx.h"
 #include "mx_kernels.h"
@@ -61,6 +62,18 @@ mx_status check_common(int fmt, int block, int64_t rows, int64_t cols, bool* not
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_DEVICE; }
 
+// Test hook: with MX_TEST_FAIL_LAUNCH=1 in the environment (read once per
+// process), every call that passes its argument checks returns
+// MX_ERR_DEVICE instead of launching, so a caller's handling of device
+// errors can be exercised on a machine without a GPU.
+bool forced_launch_failure() {
+  static const bool fail = [] {
+    const char* e = getenv("MX_TEST_FAIL_LAUNCH");
+    return e != nullptr && e[0] == '1' && e[1] == '\0';
+  }();
+  return fail;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,6 +113,7 @@ mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype, const void* x
   if (nothing) return MX_OK;
   if (!x || !codes || !scales || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
     return from_hip(mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype == MX_BF16, x,
@@ -118,6 +132,7 @@ mx_status mx_dequantize(mx_format fmt, int block, const void* codes, const uint8
   if (nothing) return MX_OK;
   if (!codes || !scales || !y || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
   if (!aligned16(codes) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
     return from_hip(mxk::launch_exmy(1, exmy_width(fmt), exmy_params(fmt), out_dtype == MX_BF16,
@@ -135,6 +150,7 @@ mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype, const void*
   if (nothing) return MX_OK;
   if (!x || !y) return MX_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
     return from_hip(mxk::launch_exmy(2, exmy_width(fmt), exmy_params(fmt), dtype == MX_BF16, x,
@@ -152,6 +168,7 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float* s, int64_t 
   if (nothing) return MX_OK;
   if (!s || !codes || !scales) return MX_ERR_NULL;
   if (!aligned16(s) || !aligned16(codes)) return MX_ERR_ALIGN;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
   return from_hip(mxk::launch_softmax_quantize(fmt, s, rows, cols, codes, scales,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -180,6 +197,7 @@ mx_status attention(bool efq, mx_format v_fmt, int block, const void* q, const v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v_codes) || !aligned16(o) ||
       (p_codes && !aligned16(p_codes)))
     return MX_ERR_ALIGN;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
   return from_hip(mxk::launch_attention(v_fmt, efq, out_dtype == MX_BF16, q, k, v_codes,
                                         v_scales, (int)heads, (int)lq, (int)lk, scale, o, row_max,
                                         row_sum, p_codes, p_scales,

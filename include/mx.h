@@ -54,7 +54,10 @@
  * is the default stream).  Argument errors are found on the host before
  * anything is enqueued and returned synchronously; a launch failure returns
  * MX_ERR_DEVICE.  rows == 0 or cols == 0 is a no-op returning MX_OK.  The
- * library allocates nothing and keeps no state between calls.
+ * library allocates nothing and keeps no state between calls.  Test hook:
+ * with MX_TEST_FAIL_LAUNCH=1 in the process environment (read at the first
+ * call), a call that passes its argument checks returns MX_ERR_DEVICE
+ * without launching anything.
  */
 #ifndef MX_H
 #define MX_H

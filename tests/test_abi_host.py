@@ -159,3 +159,46 @@ def test_attention_argument_errors(mx):
     assert call(lq=0, q=None, k=None, vc=None, vs=None, o=None) == OK
     for f in (E4M3, E2M3, E3M2, E2M1):
         assert call(v_fmt=f, heads=0) == OK
+
+
+FORCED_FAILURE_CHILD = r"""
+import block_scaled_bit_amd as mx
+A = 1 << 20  # fake 16-byte-aligned addresses: the hook returns before any launch
+DEV, OK, SHAPE, NULL = 5, 0, 2, 1
+got = {
+    "quantize": mx.mx_quantize(0, 32, 0, A, 4, 32, A, A, None, stream=0),
+    "quantize_exmy": mx.mx_quantize(mx.MX_EXMY(3, 3), 32, 1, A, 4, 32, A, A, None, stream=0),
+    "dequantize": mx.mx_dequantize(3, 32, A, A, None, 4, 32, 1, A, stream=0),
+    "fake_quantize": mx.mx_fake_quantize(4, 32, 0, A, A, 4, 32, stream=0),
+    "softmax_quantize": mx.mx_softmax_quantize(2, 32, A, 4, 64, A, A, stream=0),
+    "attention": mx.mx_attention_fwd(3, 32, A, A, A, A, 2, 64, 128, 128, 0.125, 0, A,
+                                     None, None, None, None, stream=0),
+    "attention_efq": mx.mx_attention_fwd_efq(3, 32, A, A, A, A, 2, 64, 128, 128, 0.125, 0, A,
+                                             None, None, None, None, stream=0),
+    # argument errors are still found first, and empty work is still a no-op
+    "bad_shape": mx.mx_quantize(0, 32, 0, A, 4, 31, A, A, None, stream=0),
+    "null": mx.mx_dequantize(0, 32, None, A, None, 4, 32, 0, A, stream=0),
+    "empty": mx.mx_quantize(0, 32, 0, None, 0, 32, None, None, None, stream=0),
+}
+want = {k: DEV for k in got}
+want.update(bad_shape=SHAPE, null=NULL, empty=OK)
+assert got == want, got
+try:
+    mx._check(mx.mx_quantize(0, 32, 0, A, 4, 32, A, A, None, stream=0), "mx_quantize")
+except mx.MxError as e:
+    assert e.status == DEV and "launch failed" in str(e)
+else:
+    raise AssertionError("no MxError")
+print("forced failure ok")
+"""
+
+
+def test_forced_launch_failure_returns_device_error():
+    # MX_TEST_FAIL_LAUNCH=1 (read once per process) turns every call that
+    # passes its argument checks into MX_ERR_DEVICE without a launch; run in
+    # a child process so no other test sees the hook
+    env = dict(os.environ, MX_TEST_FAIL_LAUNCH="1")
+    r = subprocess.run(["python", "-c", FORCED_FAILURE_CHILD], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "forced failure ok" in r.stdout
