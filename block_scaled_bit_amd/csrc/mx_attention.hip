@@ -197,7 +197,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
   __shared__ uint8_t vsc0[kD * 2], vsc1[kD * 2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index through readfirstlane is known to be uniform, so the LDS
+  // destinations of the direct loads (and all that depends only on the
+  // wave) stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, h = lane >> 5;
 
   // Workgroup order: the hardware deals consecutive workgroups round-robin
