@@ -37,6 +37,8 @@ CACHE_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30
 METRIC = "MX quantize+pack GB/s and % of HBM peak, bf16 14336×4096 → MXFP6 E2M3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# seconds of untimed launches before each secondary line (clock ramp-up)
+SECONDARY_WARM_S = 0.2
 CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
 
 
@@ -64,14 +66,24 @@ def rotation_sets(bytes_per_set: int) -> int:
     return max(2, -(-ROTATE_BYTES // bytes_per_set))
 
 
-def time_launches(fn, nsets, steps, warmup):
+def time_launches(fn, nsets, steps, warmup, min_warm_s=0.0):
     """Average device time per launch (ms) over `steps` back-to-back launches,
-    measured with HIP events on the stream the launches go to."""
+    measured with HIP events on the stream the launches go to.  At least
+    `warmup` untimed launches come first, and more until `min_warm_s`
+    seconds have passed: after an idle gap (host-side input generation) the
+    GPU takes a while under load to return to its steady clock."""
+    import time
     import torch
     torch.cuda.synchronize()
     for i in range(warmup):
         fn(i % nsets)
     torch.cuda.synchronize()
+    t_start, i = time.perf_counter(), warmup
+    while time.perf_counter() - t_start < min_warm_s:
+        for _ in range(8):
+            fn(i % nsets)
+            i += 1
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -114,7 +126,7 @@ def headline(mx, x_np, steps, warmup):
     def copy(i):
         xs[(i + 1) % nsets].copy_(xs[i])
 
-    ms_copy = time_launches(copy, nsets, max(50, steps // 10), 20)
+    ms_copy = time_launches(copy, nsets, max(50, steps // 10), 20, min_warm_s=SECONDARY_WARM_S)
     copy_gbs = 2 * in_bytes / ms_copy / 1e6
     return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs
 
@@ -142,17 +154,21 @@ def secondary(mx, steps):
     cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     for f, nm in ((1, "e3m2"), (0, "e2m3")):
-        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3)
+        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3,
+                           min_warm_s=SECONDARY_WARM_S)
         if f == 1:
             record("quantize_e3m2", ms, rows * cols * 2, nb * 25, "linear_weight bf16 14336x4096")
-        ms = time_launches(lambda i: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+        ms = time_launches(lambda i: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
+                           min_warm_s=SECONDARY_WARM_S)
         record(f"dequantize_{nm}_to_bf16", ms, nb * 25, rows * cols * 2, "linear_weight bf16 14336x4096")
     # a generic eXmY format (7-bit e3m3, 28 B per block; rounding in fp32)
     g = mx.MX_EXMY(3, 3)
     cg = [torch.empty(nb * 28, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_quantize(g, 32, 0, xs[i], rows, cols, cg[i], ss[i], None, stream), n, k, 3)
+    ms = time_launches(lambda i: mx.mx_quantize(g, 32, 0, xs[i], rows, cols, cg[i], ss[i], None, stream), n, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("quantize_exmy_e3m3", ms, rows * cols * 2, nb * 29, "linear_weight bf16 14336x4096")
-    ms = time_launches(lambda i: mx.mx_dequantize(g, 32, cg[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+    ms = time_launches(lambda i: mx.mx_dequantize(g, 32, cg[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("dequantize_exmy_e3m3_to_bf16", ms, nb * 29, rows * cols * 2, "linear_weight bf16 14336x4096")
     del xs, cs, ss, cg
 
@@ -163,12 +179,14 @@ def secondary(mx, steps):
     n = rotation_sets(rows * cols * 4)
     xs = bf16_dev(a, n)
     ys = [torch.empty_like(xs[0]) for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_fake_quantize(4, 32, 0, xs[i], ys[i], rows, cols, stream), n, k, 3)
+    ms = time_launches(lambda i: mx.mx_fake_quantize(4, 32, 0, xs[i], ys[i], rows, cols, stream), n, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("fake_quantize_axs6", ms, rows * cols * 2, rows * cols * 2, "axs6_weight bf16 4096x4096")
     cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     aa = [torch.empty((nb + 3) // 4, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_quantize(4, 32, 0, xs[i], rows, cols, cs[i], ss[i], aa[i], stream), n, k, 3)
+    ms = time_launches(lambda i: mx.mx_quantize(4, 32, 0, xs[i], rows, cols, cs[i], ss[i], aa[i], stream), n, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("quantize_axs6", ms, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, "axs6_weight bf16 4096x4096")
     del xs, ys, cs, ss, aa
 
@@ -181,9 +199,11 @@ def secondary(mx, steps):
     cs = [torch.empty(nb * 32, dtype=torch.uint8, device="cuda") for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     for f, nm, bpb in ((3, "e4m3", 32), (0, "e2m3", 24)):
-        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3)
+        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3,
+                           min_warm_s=SECONDARY_WARM_S)
         record(f"quantize_{nm}_activations", ms, rows * cols * 2, nb * (bpb + 1), "activations bf16 16384x8192")
-    ms = time_launches(lambda i: mx.mx_dequantize(3, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3)
+    ms = time_launches(lambda i: mx.mx_dequantize(3, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("dequantize_e4m3_activations", ms, nb * 33, rows * cols * 2, "activations bf16 16384x8192")
     del xs, cs, ss
 
@@ -195,9 +215,11 @@ def secondary(mx, steps):
     del s
     c = torch.empty(nb * 16, dtype=torch.uint8, device="cuda")
     sc = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    ms = time_launches(lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream), 1, max(5, k // 4), 2)
+    ms = time_launches(lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream), 1, max(5, k // 4), 2,
+                       min_warm_s=SECONDARY_WARM_S)
     record("softmax_quantize_e2m1", ms, rows * cols * 4, nb * 17, "attn_scores fp32 32x4096x4096")
-    ms = time_launches(lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, 1, sd, stream), 1, max(5, k // 4), 2)
+    ms = time_launches(lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, 1, sd, stream), 1, max(5, k // 4), 2,
+                       min_warm_s=SECONDARY_WARM_S)
     record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
     del sd, c, sc
 
@@ -242,7 +264,8 @@ def secondary(mx, steps):
     cc = torch.empty(1024 * 24, dtype=torch.uint8, device="cuda")
     s1 = torch.empty(1024, dtype=torch.uint8, device="cuda")
     yy = torch.empty_like(xsm)
-    ms = time_launches(lambda i: mx.mx_quantize(0, 32, 1, xsm, 128, 256, cc, s1, None, stream), 1, k, 3)
+    ms = time_launches(lambda i: mx.mx_quantize(0, 32, 1, xsm, 128, 256, cc, s1, None, stream), 1, k, 3,
+                       min_warm_s=SECONDARY_WARM_S)
     record("quantize_e2m3_weights_small", ms, 131072, 25600, "weights_small fp32 128x256 (launch-bound)")
     return res
 
@@ -276,7 +299,7 @@ def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
             if st:
                 raise mx.MxError(st, "attention forward")
 
-        ms = time_launches(step, 1, max(10, k // 4), 5)
+        ms = time_launches(step, 1, max(10, k // 4), 5, min_warm_s=SECONDARY_WARM_S)
         out[name] = {
             "us": round(ms * 1e3, 2), "TFLOPs": round(flops / ms / 1e9, 1),
             "Gscores_per_s": round(scores / ms / 1e6, 1),
@@ -334,7 +357,7 @@ def copy_calibration(steps):
     n = 163315712
     a = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
     b = torch.empty_like(a)
-    ms = time_launches(lambda i: b.copy_(a), 1, steps, 3)
+    ms = time_launches(lambda i: b.copy_(a), 1, steps, 3, min_warm_s=SECONDARY_WARM_S)
     print(json.dumps({"copy_bytes_each_way": n, "us": round(ms * 1e3, 2),
                       "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
 
