@@ -17,7 +17,7 @@ import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
 __all__ = [
     "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
     "FORMATS", "MX_EXMY", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
-    "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd",
+    "mx_quantize_batch", "quantize_many", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd",
     "mx_attention_fwd_efq", "quantize",
     "dequantize", "fake_quantize", "softmax_quantize", "quantize_v", "attention_fwd",
     "library_path",
@@ -56,6 +56,12 @@ class MxError(RuntimeError):
         self.status = status
 
 
+class _TensorDesc(ctypes.Structure):
+    """mx_tensor_desc of include/mx.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("aux", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(library_path):
         raise ImportError(
@@ -68,13 +74,14 @@ def _load():
     lib.mx_status_str.restype = ctypes.c_char_p
     lib.mx_buffer_sizes.argtypes = [I, I, I64, I64, P, P, P]
     lib.mx_quantize.argtypes = [I, I, I, P, I64, I64, P, P, P, P]
+    lib.mx_quantize_batch.argtypes = [I, I, I, ctypes.POINTER(_TensorDesc), I, P]
     lib.mx_dequantize.argtypes = [I, I, P, P, P, I64, I64, I, P, P]
     lib.mx_fake_quantize.argtypes = [I, I, I, P, P, I64, I64, P]
     lib.mx_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P, P]
     lib.mx_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I, P,
                                      P, P, P, P, P]
     lib.mx_attention_fwd_efq.argtypes = lib.mx_attention_fwd.argtypes
-    for f in ("mx_buffer_sizes", "mx_quantize", "mx_dequantize", "mx_fake_quantize",
+    for f in ("mx_buffer_sizes", "mx_quantize", "mx_quantize_batch", "mx_dequantize", "mx_fake_quantize",
               "mx_softmax_quantize", "mx_attention_fwd", "mx_attention_fwd_efq"):
         getattr(lib, f).restype = I
     return lib
@@ -138,6 +145,16 @@ def mx_buffer_sizes(fmt, block: int, rows: int, cols: int):
 def mx_quantize(fmt, block, in_dtype, x, rows, cols, codes, scales, aux, stream=None) -> int:
     return _lib.mx_quantize(_fmt(fmt), block, in_dtype, _ptr(x), rows, cols, _ptr(codes),
                             _ptr(scales), _ptr(aux), _stream(stream))
+
+
+def mx_quantize_batch(fmt, block, in_dtype, tensors, stream=None) -> int:
+    """tensors: a sequence of (x, rows, cols, codes, scales, aux) with
+    tensors, int addresses or None, as mx_quantize takes them."""
+    tensors = list(tensors)
+    arr = (_TensorDesc * max(1, len(tensors)))()
+    for i, (x, rows, cols, codes, scales, aux) in enumerate(tensors):
+        arr[i] = _TensorDesc(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(aux))
+    return _lib.mx_quantize_batch(_fmt(fmt), block, in_dtype, arr, len(tensors), _stream(stream))
 
 
 def mx_dequantize(fmt, block, codes, scales, aux, rows, cols, out_dtype, y, stream=None) -> int:
@@ -206,6 +223,31 @@ def quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK):
            if f == MX_AXS6 else None)
     _check(mx_quantize(f, block, _dtype_code(x), x, rows, cols, codes, scales, aux), "mx_quantize")
     return codes, scales, aux
+
+
+def quantize_many(xs, fmt="mxfp6_e2m3", block: int = BLOCK):
+    """quantize() of every tensor in xs (one format and input dtype) through
+    mx_quantize_batch: a list of (codes, scales, aux)."""
+    f = _fmt(fmt)
+    xs = list(xs)
+    if not xs:
+        return []
+    dt = _dtype_code(xs[0])
+    outs, descs = [], []
+    for x in xs:
+        if _dtype_code(x) != dt:
+            raise ValueError("quantize_many takes tensors of one dtype")
+        rows, cols = _rows_cols(x)
+        nbr = cols // BLOCK if cols % BLOCK == 0 else 0
+        lead = tuple(x.shape[:-1])
+        codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=x.device)
+        aux = (torch.empty(((rows * nbr) + 3) // 4, dtype=torch.uint8, device=x.device)
+               if f == MX_AXS6 else None)
+        outs.append((codes, scales, aux))
+        descs.append((x, rows, cols, codes, scales, aux))
+    _check(mx_quantize_batch(f, block, dt, descs), "mx_quantize_batch")
+    return outs
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, aux=None, fmt="mxfp6_e2m3",

@@ -104,22 +104,100 @@ mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
   return MX_OK;
 }
 
+namespace {
+
+// The argument checks of one quantize call; *nothing = true for an empty
+// tensor (a no-op).
+mx_status quantize_args(int fmt, int block, int in_dtype, const void* x, int64_t rows,
+                        int64_t cols, const void* codes, const uint8_t* scales,
+                        const uint8_t* aux, bool* nothing) {
+  mx_status st = check_common(fmt, block, rows, cols, nothing);
+  if (st != MX_OK) return st;
+  if (!dtype_ok(in_dtype)) return MX_ERR_UNSUPPORTED;
+  if (*nothing) return MX_OK;
+  if (!x || !codes || !scales || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+// One checked, non-empty tensor.
+hipError_t quantize_one(int fmt, int in_dtype, const void* x, int64_t rows, int64_t cols,
+                        void* codes, uint8_t* scales, uint8_t* aux, hipStream_t st) {
+  const int64_t nb = rows * (cols / MX_BLOCK);
+  if (is_exmy(fmt))
+    return mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype == MX_BF16, x,
+                            nullptr, nb, codes, scales, st);
+  return mxk::launch_quantize(fmt, in_dtype == MX_BF16, x, nb, codes, scales, aux, st);
+}
+
+}  // namespace
+
 mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype, const void* x, int64_t rows,
                       int64_t cols, void* codes, uint8_t* scales, uint8_t* aux, void* stream) {
   bool nothing = false;
-  mx_status st = check_common(fmt, block, rows, cols, &nothing);
-  if (st != MX_OK) return st;
-  if (!dtype_ok(in_dtype)) return MX_ERR_UNSUPPORTED;
-  if (nothing) return MX_OK;
-  if (!x || !codes || !scales || (fmt == MX_AXS6 && !aux)) return MX_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes)) return MX_ERR_ALIGN;
+  const mx_status st = quantize_args(fmt, block, in_dtype, x, rows, cols, codes, scales, aux,
+                                     &nothing);
+  if (st != MX_OK || nothing) return st;
   if (forced_launch_failure()) return MX_ERR_DEVICE;
-  const int64_t nb = rows * (cols / MX_BLOCK);
-  if (is_exmy(fmt))
-    return from_hip(mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype == MX_BF16, x,
-                                     nullptr, nb, codes, scales, static_cast<hipStream_t>(stream)));
-  return from_hip(mxk::launch_quantize(fmt, in_dtype == MX_BF16, x, nb, codes, scales, aux,
-                                       static_cast<hipStream_t>(stream)));
+  return from_hip(quantize_one(fmt, in_dtype, x, rows, cols, codes, scales, aux,
+                               static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_quantize_batch(mx_format fmt, int block, mx_dtype in_dtype,
+                            const mx_tensor_desc* tensors, int count, void* stream) {
+  if (count < 0) return MX_ERR_SHAPE;
+  if (count > 0 && !tensors) return MX_ERR_NULL;
+  // every tensor is checked before anything is enqueued
+  int nonempty = 0;
+  for (int i = 0; i < count; ++i) {
+    const mx_tensor_desc& t = tensors[i];
+    bool nothing = false;
+    const mx_status st = quantize_args(fmt, block, in_dtype, t.x, t.rows, t.cols, t.codes,
+                                       t.scales, t.aux, &nothing);
+    if (st != MX_OK) return st;
+    nonempty += nothing ? 0 : 1;
+  }
+  if (nonempty == 0) return MX_OK;
+  if (forced_launch_failure()) return MX_ERR_DEVICE;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool grouped = fmt >= MX_FP6_E2M3 && fmt <= MX_FP8_E4M3;
+  // MX hardware formats: up to kBatchMax tensors per launch, each tensor's
+  // blocks in whole workgroups of 256; a launch stays under 2^31
+  // workgroups, and a tensor too large for that goes alone
+  constexpr int64_t kMaxWgs = 0x7FFFFFFF;
+  mxk::QuantBatch a{};
+  a.n = 0;
+  a.wg_start[0] = 0;
+  auto flush = [&]() -> hipError_t {
+    if (a.n == 0) return hipSuccess;
+    const hipError_t e = mxk::launch_quantize_batch(fmt, in_dtype == MX_BF16, a, hs);
+    a.n = 0;
+    a.wg_start[0] = 0;
+    return e;
+  };
+  for (int i = 0; i < count; ++i) {
+    const mx_tensor_desc& t = tensors[i];
+    if (t.rows == 0 || t.cols == 0) continue;
+    const int64_t nb = t.rows * (t.cols / MX_BLOCK);
+    const int64_t wgs = (nb + 255) / 256;
+    if (!grouped || wgs > kMaxWgs / 2) {
+      hipError_t e = flush();
+      if (e == hipSuccess)
+        e = quantize_one(fmt, in_dtype, t.x, t.rows, t.cols, t.codes, t.scales, t.aux, hs);
+      if (e != hipSuccess) return MX_ERR_DEVICE;
+      continue;
+    }
+    if (a.n == mxk::kBatchMax || (int64_t)a.wg_start[a.n] + wgs > kMaxWgs) {
+      if (flush() != hipSuccess) return MX_ERR_DEVICE;
+    }
+    a.x[a.n] = t.x;
+    a.codes[a.n] = t.codes;
+    a.scales[a.n] = t.scales;
+    a.nb[a.n] = nb;
+    a.wg_start[a.n + 1] = (uint32_t)(a.wg_start[a.n] + wgs);
+    ++a.n;
+  }
+  return from_hip(flush());
 }
 
 mx_status mx_dequantize(mx_format fmt, int block, const void* codes, const uint8_t* scales,

@@ -27,6 +27,22 @@ struct ExmyParams {
 
 hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
                            uint8_t* scales, uint8_t* aux, hipStream_t st);
+
+// Up to kBatchMax tensors of one MX hardware format (E2M3, E3M2, E2M1,
+// E4M3) quantized by one launch, passed by value as the kernel argument:
+// tensor i has nb[i] > 0 blocks and owns workgroups [wg_start[i],
+// wg_start[i + 1]) of 256 blocks each; wg_start[0] = 0 and wg_start[n] is
+// the grid size.
+constexpr int kBatchMax = 16;
+struct QuantBatch {
+  int n;
+  uint32_t wg_start[kBatchMax + 1];
+  int64_t nb[kBatchMax];
+  const void* x[kBatchMax];
+  void* codes[kBatchMax];
+  uint8_t* scales[kBatchMax];
+};
+hipError_t launch_quantize_batch(int fmt, bool bf16, const QuantBatch& a, hipStream_t st);
 hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
                              const uint8_t* aux, int64_t nb, void* y, hipStream_t st);
 hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,

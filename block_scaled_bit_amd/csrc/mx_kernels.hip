@@ -138,33 +138,54 @@ __device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void
 // ---------------------------------------------------------------------------
 // MX formats (E2M3, E3M2, E2M1, E4M3): hardware conversions
 // ---------------------------------------------------------------------------
+// Block b of one tensor: scale byte, codes, and both stores.
+template <int F, bool BF16>
+__device__ __forceinline__ void quantize_mx_block(const void* __restrict__ x, int64_t b,
+                                                  void* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  constexpr int W = Fmt<F>::W;
+  uint32_t o[W];
+  uint32_t byte;
+  if constexpr (BF16) {
+    uint32_t d[16];
+    load_bf16_block(x, b, d);
+    byte = scale_byte_from_amax<F>(amax_bf16x32(d));
+    encode_bf16<F>(d, scale_operand(byte), o);
+  } else {
+    uint32_t d[32];
+    load_f32_block(x, b, d);
+    byte = scale_byte_from_amax<F>(amax_f32x32(d));
+    encode_f32<F>(d, scale_operand(byte), o);
+  }
+  if (byte == 0xFFu) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) o[k] = 0u;
+  }
+  store_codes<W>(codes, b, o);
+  scales[b] = (uint8_t)byte;
+}
+
 template <int F, bool BF16>
 __global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, int64_t nb,
                                                    void* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
-  constexpr int W = Fmt<F>::W;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-    uint32_t o[W];
-    uint32_t byte;
-    if constexpr (BF16) {
-      uint32_t d[16];
-      load_bf16_block(x, b, d);
-      byte = scale_byte_from_amax<F>(amax_bf16x32(d));
-      encode_bf16<F>(d, scale_operand(byte), o);
-    } else {
-      uint32_t d[32];
-      load_f32_block(x, b, d);
-      byte = scale_byte_from_amax<F>(amax_f32x32(d));
-      encode_f32<F>(d, scale_operand(byte), o);
-    }
-    if (byte == 0xFFu) {
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride)
+    quantize_mx_block<F, BF16>(x, b, codes, scales);
+}
+
+// Several tensors in one launch: workgroup w belongs to the tensor i with
+// wg_start[i] <= w < wg_start[i + 1] (found from blockIdx and the kernel
+// arguments alone, so i is uniform and its pointers are scalar loads), and
+// its lanes take blocks 256 (w - wg_start[i]) + lane of that tensor.
+template <int F, bool BF16>
+__global__ __launch_bounds__(256) void quantize_mx_batch(const QuantBatch a) {
+  const uint32_t w = blockIdx.x;
+  int i = 0;
 #pragma unroll
-      for (int k = 0; k < W; ++k) o[k] = 0u;
-    }
-    store_codes<W>(codes, b, o);
-    scales[b] = (uint8_t)byte;
-  }
+  for (int k = 1; k < kBatchMax; ++k) i = (k < a.n && w >= a.wg_start[k]) ? k : i;
+  const int64_t b = (int64_t)(w - a.wg_start[i]) * 256 + threadIdx.x;
+  if (b < a.nb[i]) quantize_mx_block<F, BF16>(a.x[i], b, a.codes[i], a.scales[i]);
 }
 
 template <int F, bool BF16>
@@ -780,6 +801,16 @@ hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* 
   MXK_SWITCH_MX(fmt, {
     if (bf16) hipLaunchKernelGGL((quantize_mx<FF, true>), grid, block, 0, st, x, nb, codes, scales);
     else hipLaunchKernelGGL((quantize_mx<FF, false>), grid, block, 0, st, x, nb, codes, scales);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(int fmt, bool bf16, const QuantBatch& a, hipStream_t st) {
+  if (a.n < 1 || a.n > kBatchMax) return hipErrorInvalidValue;
+  const dim3 grid(a.wg_start[a.n]), block(256);
+  MXK_SWITCH_MX(fmt, {
+    if (bf16) hipLaunchKernelGGL((quantize_mx_batch<FF, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((quantize_mx_batch<FF, false>), grid, block, 0, st, a);
   });
   return hipGetLastError();
 }

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 3
+#define MX_ABI_VERSION 4
 #define MX_BLOCK 32
 
 typedef enum {
@@ -121,6 +121,30 @@ mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
 mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype,
                       const void *x, int64_t rows, int64_t cols, void *codes,
                       uint8_t *scales, uint8_t *aux, void *stream);
+
+/* One tensor of mx_quantize_batch: the arguments mx_quantize takes for it. */
+typedef struct mx_tensor_desc {
+  const void *x;   /* [rows, cols] of the batch's in_dtype, 16-byte aligned */
+  int64_t rows;
+  int64_t cols;    /* multiple of 32 */
+  void *codes;     /* [rows, cols/32, bpb], 16-byte aligned */
+  uint8_t *scales; /* [rows, cols/32] */
+  uint8_t *aux;    /* AXS-6 only, as for mx_quantize; else ignored */
+} mx_tensor_desc;
+
+/* Quantize + pack `count` tensors of one format and input type, with the
+ * results mx_quantize gives for each (the conversion of a model layer by
+ * layer, "Online MXFP6", "Start a model").  The MX hardware formats (E2M3,
+ * E3M2, E2M1, E4M3) take up to 16 tensors per launch, so small tensors
+ * share the GPU instead of each paying a launch and its tail; AXS-6 and
+ * eXmY are launched tensor by tensor.  `tensors` is a host array read only
+ * during the call.  Every tensor is checked before anything is enqueued;
+ * the first failing one's status is returned (count < 0: MX_ERR_SHAPE;
+ * tensors NULL with count > 0: MX_ERR_NULL).  Empty tensors are skipped;
+ * outputs of different tensors must not overlap. */
+mx_status mx_quantize_batch(mx_format fmt, int block, mx_dtype in_dtype,
+                            const mx_tensor_desc *tensors, int count,
+                            void *stream);
 
 /* Dequantize: codes + scales (+ aux) -> y [rows, cols] of out_dtype. */
 mx_status mx_dequantize(mx_format fmt, int block, const void *codes,

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mx_quantize", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize",
               "mx_buffer_sizes", "mx_status_str", "mx_abi_version", "mx_attention_fwd",
-              "mx_attention_fwd_efq"):
+              "mx_attention_fwd_efq", "mx_quantize_batch"):
         assert f in names
 
 
@@ -51,7 +51,7 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 3
+    assert mx.mx_abi_version() == 4
     for s in range(0, 7):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
@@ -103,6 +103,27 @@ def test_other_entry_points_argument_errors(mx):
     assert mx.mx_softmax_quantize(2, 32, A, 4, 30, A, A, stream=0) == SHAPE
     assert mx.mx_softmax_quantize(2, 32, None, 4, 32, A, A, stream=0) == NULL
     assert mx.mx_softmax_quantize(2, 32, None, 0, 32, None, None, stream=0) == OK
+
+
+def test_quantize_batch_argument_errors(mx):
+    import ctypes
+    good = (A, 4, 64, A, A, None)
+    lib = mx._lib
+    assert lib.mx_quantize_batch(0, 32, 0, None, -1, None) == SHAPE
+    assert lib.mx_quantize_batch(0, 32, 0, None, 2, None) == NULL
+    assert lib.mx_quantize_batch(0, 32, 0, None, 0, None) == OK
+    assert mx.mx_quantize_batch(0, 32, 0, [], stream=0) == OK
+    # the first failing tensor's status, wherever it is in the batch
+    assert mx.mx_quantize_batch(0, 32, 0, [good, (A, 4, 48, A, A, None)], stream=0) == SHAPE
+    assert mx.mx_quantize_batch(0, 32, 0, [good, good, (A, 4, 64, None, A, None)], stream=0) == NULL
+    assert mx.mx_quantize_batch(0, 32, 0, [(A + 8, 4, 64, A, A, None), good], stream=0) == ALIGN
+    assert mx.mx_quantize_batch(4, 32, 0, [good], stream=0) == NULL       # AXS-6 needs aux
+    assert mx.mx_quantize_batch(0, 16, 0, [good], stream=0) == UNSUP
+    assert mx.mx_quantize_batch(0, 32, 3, [good], stream=0) == UNSUP
+    assert mx.mx_quantize_batch(0x200, 32, 0, [good], stream=0) == UNSUP
+    # empty tensors only: nothing to do, even with NULL pointers
+    assert mx.mx_quantize_batch(0, 32, 0, [(None, 0, 64, None, None, None)] * 3, stream=0) == OK
+    assert ctypes.sizeof(mx._TensorDesc) == 48
 
 
 def test_python_helpers_reject_host_tensors(mx):
@@ -173,6 +194,8 @@ got = {
     "softmax_quantize": mx.mx_softmax_quantize(2, 32, A, 4, 64, A, A, stream=0),
     "attention": mx.mx_attention_fwd(3, 32, A, A, A, A, 2, 64, 128, 128, 0.125, 0, A,
                                      None, None, None, None, stream=0),
+    "quantize_batch": mx.mx_quantize_batch(2, 32, 0, [(A, 4, 64, A, A, None)] * 20, stream=0),
+    "quantize_batch_exmy": mx.mx_quantize_batch(0x133, 32, 0, [(A, 4, 64, A, A, None)], stream=0),
     "attention_efq": mx.mx_attention_fwd_efq(3, 32, A, A, A, A, 2, 64, 128, 128, 0.125, 0, A,
                                              None, None, None, None, stream=0),
     # argument errors are still found first, and empty work is still a no-op
