@@ -1,6 +1,9 @@
 /*
  * mxref.c -- plain, slow, obviously-correct CPU oracle for block-shared-
- * exponent quantization (MXFP6 E2M3/E3M2, MXFP4 E2M1, MXFP8 E4M3, AXS-6).
+ * exponent quantization (MXFP6 E2M3/E3M2, MXFP4 E2M1, MXFP8 E4M3, AXS-6 and
+ * the generic eXmY formats), the exp-then-quantize probabilities, and the
+ * attention forward whose probabilities are E2M1 blocks (exp-then-quantize,
+ * or EFQ's exp-free rule).
  *
  * TEST INFRASTRUCTURE ONLY (see mxref.h).  Built with gcc -O2
  * -ffp-contract=off, no fast-math.  Every rule below cites the page it
@@ -15,9 +18,14 @@
  *
  * Parity pins: format tables, scale rule, RNE/saturation, packing and
  * dequantization are pinned by the CPU tests (library dtypes, brute-force
- * nearest-code search, closed-form invariants).  The NaN/inf block rule,
- * the bit order inside a packed block and the AXS-6 element/config
- * semantics are readings of silent passages: parity unpinned by the pages,
+ * nearest-code search, closed-form invariants); the eXmY grids by field
+ * enumeration, library dtypes and closed forms; the fixed exp by a
+ * reference exponential within its error bound; the attention forward by
+ * closed forms (equal scores, a dominant key), brute-force probability
+ * blocks and an error bound against exact attention.  The NaN/inf block
+ * rule, the bit order inside a packed block and the AXS-6 element/config
+ * semantics are readings of silent passages, and EFQ's affine rule is a
+ * reading with no constants on the pages: parity unpinned by the pages,
  * pinned only by the written rules here and their unit tests.
  */
 #include "mxref.h"

@@ -1,6 +1,7 @@
 /*
- * mxref.h -- plain CPU oracle for block-shared-exponent (MX / AXS-6)
- * quantization.
+ * mxref.h -- plain CPU oracle for block-shared-exponent (MX / AXS-6 /
+ * eXmY) quantization, exp-then-quantize probabilities and the attention
+ * forward with E2M1 probabilities.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link
  * or call this; only the test-suite, the smoke check and the CPU-baseline
@@ -15,7 +16,7 @@
  *   x        [rows, cols]          bf16 bit patterns (uint16) or fp32
  *   codes    [rows, cols/32, bpb]  packed element codes, bpb bytes/block
  *                                  (24 for FP6 and AXS-6, 16 for FP4,
- *                                  32 for FP8)
+ *                                  32 for FP8, 4w for eXmY of width w)
  *   scales   [rows, cols/32]       one E8M0 byte per block (AXS-6: the
  *                                  8-bit shared exponent, same encoding)
  *   aux      [ceil(nblocks/4)]     AXS-6 only: 2-bit config per block,
