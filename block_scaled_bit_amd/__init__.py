@@ -2,9 +2,10 @@
 
 The functions named ``mx_*`` mirror the C ABI of ``include/mx.h`` one for one
 (argument marshalling only: torch tensors become device pointers, the
-current torch stream becomes the HIP stream).  ``quantize``, ``dequantize``,
-``fake_quantize`` and ``softmax_quantize`` additionally allocate their
-outputs with torch.  All arithmetic runs in the HIP kernels; if the library
+current torch stream becomes the HIP stream).  ``quantize``,
+``quantize_many``, ``dequantize``, ``fake_quantize``, ``softmax_quantize``,
+``quantize_v`` and ``attention_fwd`` additionally allocate their outputs
+with torch.  All arithmetic runs in the HIP kernels; if the library
 is not built this module raises at import time instead of falling back.
 """
 from __future__ import annotations

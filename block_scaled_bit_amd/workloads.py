@@ -19,7 +19,9 @@ checkpoints, activations and attention scores, which are not available):
                  set to +inf, -inf, NaN (in turn)                (seed 5)
 
 Every generator accepts a smaller (rows, cols) so tests can run the same
-recipe at a size the oracle finishes in seconds.
+recipe at a size the oracle finishes in seconds.  ``synthetic_model`` draws
+a small decoder's named bf16 weights (dense and MoE layers, gates, norms,
+embeddings) for the conversion driver's tests.
 """
 from __future__ import annotations
 
