@@ -128,7 +128,35 @@ def headline(mx, x_np, steps, warmup):
 
     ms_copy = time_launches(copy, nsets, max(50, steps // 10), 20, min_warm_s=SECONDARY_WARM_S)
     copy_gbs = 2 * in_bytes / ms_copy / 1e6
-    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs
+
+    # the ceiling of this byte mix: a copy kernel with the quantizer's grid,
+    # loads and stores and no arithmetic (tests/hwprobe/bw_probe.hip), timed
+    # exactly like the quantizer on the same buffers
+    ms_mix = None
+    probe = mix_copy_probe()
+    if probe is not None:
+        def mix(i):
+            if probe(xs[i].data_ptr(), nb, codes[i].data_ptr(), scales[i].data_ptr(), stream):
+                raise RuntimeError("probe_mix_copy launch failed")
+
+        ms_mix = time_launches(mix, nsets, steps, warmup)
+    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, ms_mix
+
+
+def mix_copy_probe():
+    """probe_mix_copy from the test probe library, or None if it is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "tests", "hwprobe", "libcvtprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    if not hasattr(lib, "probe_mix_copy"):
+        return None
+    fn = lib.probe_mix_copy
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
 
 
 def secondary(mx, steps):
@@ -395,7 +423,8 @@ def main():
         return
 
     x = workloads.linear_weight()
-    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs = headline(mx, x, args.steps, args.warmup)
+    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs, ms_mix = headline(mx, x, args.steps,
+                                                                         args.warmup)
     achieved = alg_b / ms / 1e6
     digest = source_digest()
     out = {
@@ -424,6 +453,13 @@ def main():
                          "note": "device-to-device copy of the bf16 input (read + write "
                                  "bytes / time), same buffers and rotation"},
     }
+    if ms_mix is not None:
+        out["mix_ceiling"] = {
+            "us": round(ms_mix * 1e3, 3), "GBps": round(alg_b / ms_mix / 1e6, 1),
+            "frac_of_peak": round(alg_b / ms_mix / 1e6 / HBM_PEAK_GBS, 4),
+            "headline_frac_of_ceiling": round(ms_mix / ms, 4),
+            "note": "copy kernel with the quantizer's grid, loads and stores and no arithmetic "
+                    "(tests/hwprobe/bw_probe.hip), same buffers, rotation, warm-up and steps"}
     if not args.no_cpu_baseline:
         base, parity, nrows = cpu_baseline(x, codes0, scales0)
         out["cpu_baseline"] = base

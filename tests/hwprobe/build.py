@@ -1,4 +1,6 @@
-"""Build the test-only conversion probe library (tests/hwprobe/libcvtprobe.so)."""
+"""Build the test-only probe library (tests/hwprobe/libcvtprobe.so): the
+conversion and matrix-core probes and the byte-mix copy the benchmark
+times as its ceiling."""
 import os
 import subprocess
 
@@ -10,7 +12,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared",
            "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-o", LIB + ".tmp", os.path.join(HERE, "cvt_probe.hip"), os.path.join(HERE, "mfma_probe.hip")]
+           "-o", LIB + ".tmp", os.path.join(HERE, "cvt_probe.hip"), os.path.join(HERE, "mfma_probe.hip"),
+           os.path.join(HERE, "bw_probe.hip")]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
