@@ -140,6 +140,10 @@ def headline(mx, x_np, steps, warmup):
                 raise RuntimeError("probe_mix_copy launch failed")
 
         ms_mix = time_launches(mix, nsets, steps, warmup)
+        # the probe wrote its own bytes into the output buffers: set 0 gets
+        # the quantizer's output back for the parity check against the oracle
+        step(0)
+        torch.cuda.synchronize()
     return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, ms_mix
 
 
@@ -469,6 +473,10 @@ def main():
         torch.cuda.empty_cache()
         out["secondary"] = secondary(mx, args.steps)
     print(json.dumps(out), flush=True)
+    if out.get("parity", {}).get("bit_exact") is False:
+        print("bench.py: the GPU's codes or scales differ from the oracle's", file=sys.stderr,
+              flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
