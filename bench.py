@@ -147,6 +147,22 @@ def headline(mx, x_np, steps, warmup):
     return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, ms_mix
 
 
+def rows_floor_probe():
+    """probe_rows_floor from the test probe library, or None if it is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "tests", "hwprobe", "libcvtprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    if not hasattr(lib, "probe_rows_floor"):
+        return None
+    fn = lib.probe_rows_floor
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def mix_copy_probe():
     """probe_mix_copy from the test probe library, or None if it is not built."""
     import ctypes
@@ -250,6 +266,19 @@ def secondary(mx, steps):
     ms = time_launches(lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream), 1, max(5, k // 4), 2,
                        min_warm_s=SECONDARY_WARM_S)
     record("softmax_quantize_e2m1", ms, rows * cols * 4, nb * 17, "attn_scores fp32 32x4096x4096")
+    # its floor: the same grid, loads and stores with the arithmetic folded
+    # away (tests/hwprobe/bw_probe.hip), then the real outputs again
+    floor = rows_floor_probe()
+    if floor is not None:
+        def fl(i):
+            if floor(sd.data_ptr(), rows, cols, c.data_ptr(), sc.data_ptr(), stream):
+                raise RuntimeError("probe_rows_floor launch failed")
+
+        ms_floor = time_launches(fl, 1, max(5, k // 4), 2, min_warm_s=SECONDARY_WARM_S)
+        res["softmax_quantize_e2m1"].update(
+            floor_us=round(ms_floor * 1e3, 2), frac_of_floor=round(ms_floor / ms, 4),
+            floor_note="same grid, loads and stores with no exp or conversion")
+        mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream)
     ms = time_launches(lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, 1, sd, stream), 1, max(5, k // 4), 2,
                        min_warm_s=SECONDARY_WARM_S)
     record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
