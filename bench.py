@@ -183,7 +183,7 @@ def secondary(mx, steps):
     """Other steps of the path, each at its workload's full size."""
     import numpy as np
     import torch
-    from block_scaled_bit_amd import workloads
+    import workloads
     res = {}
     stream = torch.cuda.current_stream().cuda_stream
     k = max(10, steps // 4)
@@ -445,7 +445,7 @@ def main():
     import torch
 
     import block_scaled_bit_amd as mx
-    from block_scaled_bit_amd import workloads
+    import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.copy_calibration:

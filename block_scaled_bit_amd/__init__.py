@@ -191,6 +191,13 @@ def mx_attention_fwd_efq(v_fmt, block, q, k, v_codes, v_scales, heads, lq, lk, d
 
 # ---------------------------------------------------------------------------
 # tensor-level helpers (allocate outputs with torch)
+#
+# The C ABI takes bare pointers and cannot see buffer sizes, so every tensor
+# a helper passes down is checked here first: contiguous, of the expected
+# dtype and byte size, and on the same GPU as the first input.  The checks
+# run in that order (shape and size before the device), so a wrong buffer is
+# reported as such even for host tensors.  Any failure raises ValueError
+# before anything is launched.
 # ---------------------------------------------------------------------------
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
@@ -200,28 +207,64 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise MxError(4, f"dtype {t.dtype}")
 
 
-def _rows_cols(t: torch.Tensor):
+def _on_gpu(t: torch.Tensor, name: str, like: torch.Tensor | None = None):
     if not t.is_cuda:
-        raise ValueError("tensor must be in GPU memory (the kernels read device pointers)")
-    if t.dim() == 0:
-        raise ValueError("tensor needs at least one dimension")
+        raise ValueError(f"{name} must be in GPU memory (the kernels read device pointers)")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {like.device}")
+
+
+def _need(t, name: str, dtype: torch.dtype, nbytes: int):
+    """t must be a contiguous tensor of `dtype` holding exactly `nbytes`
+    bytes (where it lives is checked separately, after every size)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    got = t.numel() * t.element_size()
+    if got != nbytes:
+        raise ValueError(f"{name} holds {got} bytes, {nbytes} expected")
+
+
+def _rows_cols(t: torch.Tensor, name: str = "tensor"):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dim() == 0:
+        raise ValueError(f"{name} needs at least one dimension")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    _dtype_code(t)
     cols = t.shape[-1]
+    if cols % BLOCK:
+        raise ValueError(f"{name}: the last dimension ({cols}) must be a multiple of {BLOCK}")
     return (t.numel() // cols if cols else 0), cols
+
+
+def _block(block: int):
+    if block != BLOCK:
+        raise MxError(4, f"block {block}")
+
+
+def _alloc_outputs(f: int, x: torch.Tensor, rows: int, cols: int):
+    nbr = cols // BLOCK
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=x.device)
+    aux = (torch.empty(((rows * nbr) + 3) // 4, dtype=torch.uint8, device=x.device)
+           if f == MX_AXS6 else None)
+    return codes, scales, aux
 
 
 def quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK):
     """Returns (codes uint8 [.., cols/32, bpb], scales uint8 [.., cols/32],
     aux uint8 [ceil(nblocks/4)] (AXS-6) or None)."""
     f = _fmt(fmt)
-    rows, cols = _rows_cols(x)
-    nbr = cols // BLOCK if cols % BLOCK == 0 else 0
-    lead = tuple(x.shape[:-1])
-    codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=x.device)
-    scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=x.device)
-    aux = (torch.empty(((rows * nbr) + 3) // 4, dtype=torch.uint8, device=x.device)
-           if f == MX_AXS6 else None)
+    _block(block)
+    rows, cols = _rows_cols(x, "x")
+    _on_gpu(x, "x")
+    codes, scales, aux = _alloc_outputs(f, x, rows, cols)
     _check(mx_quantize(f, block, _dtype_code(x), x, rows, cols, codes, scales, aux), "mx_quantize")
     return codes, scales, aux
 
@@ -230,21 +273,20 @@ def quantize_many(xs, fmt="mxfp6_e2m3", block: int = BLOCK):
     """quantize() of every tensor in xs (one format and input dtype) through
     mx_quantize_batch: a list of (codes, scales, aux)."""
     f = _fmt(fmt)
+    _block(block)
     xs = list(xs)
     if not xs:
         return []
     dt = _dtype_code(xs[0])
-    outs, descs = [], []
-    for x in xs:
+    shapes = []
+    for i, x in enumerate(xs):
+        shapes.append(_rows_cols(x, f"xs[{i}]"))
         if _dtype_code(x) != dt:
             raise ValueError("quantize_many takes tensors of one dtype")
-        rows, cols = _rows_cols(x)
-        nbr = cols // BLOCK if cols % BLOCK == 0 else 0
-        lead = tuple(x.shape[:-1])
-        codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=x.device)
-        scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=x.device)
-        aux = (torch.empty(((rows * nbr) + 3) // 4, dtype=torch.uint8, device=x.device)
-               if f == MX_AXS6 else None)
+    outs, descs = [], []
+    for i, (x, (rows, cols)) in enumerate(zip(xs, shapes)):
+        _on_gpu(x, f"xs[{i}]", xs[0])
+        codes, scales, aux = _alloc_outputs(f, x, rows, cols)
         outs.append((codes, scales, aux))
         descs.append((x, rows, cols, codes, scales, aux))
     _check(mx_quantize_batch(f, block, dt, descs), "mx_quantize_batch")
@@ -253,23 +295,56 @@ def quantize_many(xs, fmt="mxfp6_e2m3", block: int = BLOCK):
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, aux=None, fmt="mxfp6_e2m3",
                out_dtype=torch.bfloat16, block: int = BLOCK):
+    """Inverse of quantize(): the [.., cols] tensor of out_dtype that codes,
+    scales (and, for AXS-6, aux) describe; the shape comes from scales."""
     f = _fmt(fmt)
-    if not (codes.is_cuda and scales.is_cuda):
-        raise ValueError("codes and scales must be in GPU memory")
-    lead = tuple(scales.shape[:-1])
-    cols = scales.shape[-1] * BLOCK
-    rows = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
-    y = torch.empty(lead + (cols,), dtype=out_dtype, device=codes.device)
-    _check(mx_dequantize(f, block, codes, scales, aux, rows, cols, _dtype_code(y), y),
-           "mx_dequantize")
+    _block(block)
+    if not isinstance(scales, torch.Tensor) or scales.dim() == 0:
+        raise ValueError("scales must be a tensor [.., cols/32]")
+    nbr = scales.shape[-1]
+    rows = scales.numel() // nbr if nbr else 0
+    nb = rows * nbr
+    if f not in (MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3, MX_AXS6) and \
+            (f & ~0xFF) != 0x100:
+        raise MxError(4, f"format {fmt}")
+    _need(scales, "scales", torch.uint8, nb)
+    _need(codes, "codes", torch.uint8, nb * BYTES_PER_BLOCK[f])
+    if f == MX_AXS6:
+        _need(aux, "aux", torch.uint8, (nb + 3) // 4)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise MxError(4, f"dtype {out_dtype}")
+    _on_gpu(scales, "scales")
+    _on_gpu(codes, "codes", scales)
+    if f == MX_AXS6:
+        _on_gpu(aux, "aux", scales)
+    y = torch.empty(tuple(scales.shape[:-1]) + (nbr * BLOCK,), dtype=out_dtype,
+                    device=codes.device)
+    _check(mx_dequantize(f, block, codes, scales, aux if f == MX_AXS6 else None, rows,
+                         nbr * BLOCK, _dtype_code(y), y), "mx_dequantize")
     return y
 
 
 def fake_quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK, out=None):
-    """Fused quantize->dequantize in x's dtype (out=x works in place)."""
+    """Fused quantize->dequantize in x's dtype (out=x works in place; any
+    other out must be a separate tensor of x's shape and dtype)."""
     f = _fmt(fmt)
-    rows, cols = _rows_cols(x)
-    y = torch.empty_like(x) if out is None else out
+    _block(block)
+    rows, cols = _rows_cols(x, "x")
+    if out is None:
+        _on_gpu(x, "x")
+        y = torch.empty_like(x)
+    else:
+        if not isinstance(out, torch.Tensor) or out.shape != x.shape:
+            raise ValueError("out must be a tensor of x's shape")
+        _need(out, "out", x.dtype, x.numel() * x.element_size())
+        _on_gpu(x, "x")
+        _on_gpu(out, "out", x)
+        if out.data_ptr() != x.data_ptr():
+            lo, hi = x.data_ptr(), x.data_ptr() + x.numel() * x.element_size()
+            olo, ohi = out.data_ptr(), out.data_ptr() + out.numel() * out.element_size()
+            if olo < hi and lo < ohi:
+                raise ValueError("out overlaps x without being x (only in-place use is allowed)")
+        y = out
     _check(mx_fake_quantize(f, block, _dtype_code(x), x, y, rows, cols), "mx_fake_quantize")
     return y
 
@@ -277,13 +352,12 @@ def fake_quantize(x: torch.Tensor, fmt="mxfp6_e2m3", block: int = BLOCK, out=Non
 def softmax_quantize(s: torch.Tensor, fmt="mxfp4", block: int = BLOCK):
     """P = exp(s - rowmax) per row, then block quantization of P."""
     f = _fmt(fmt)
-    if s.dtype != torch.float32:
+    _block(block)
+    if not isinstance(s, torch.Tensor) or s.dtype != torch.float32:
         raise MxError(4, "softmax_quantize needs fp32 scores")
-    rows, cols = _rows_cols(s)
-    nbr = cols // BLOCK if cols % BLOCK == 0 else 0
-    lead = tuple(s.shape[:-1])
-    codes = torch.empty(lead + (nbr, BYTES_PER_BLOCK[f]), dtype=torch.uint8, device=s.device)
-    scales = torch.empty(lead + (nbr,), dtype=torch.uint8, device=s.device)
+    rows, cols = _rows_cols(s, "s")
+    _on_gpu(s, "s")
+    codes, scales, _ = _alloc_outputs(f, s, rows, cols)
     _check(mx_softmax_quantize(f, block, s, rows, cols, codes, scales), "mx_softmax_quantize")
     return codes, scales
 
@@ -298,6 +372,9 @@ def quantize_v(v: torch.Tensor, fmt="mxfp8"):
     return codes, scales
 
 
+_V_FORMATS = (MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3)
+
+
 def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
                   v_scales: torch.Tensor, v_fmt="mxfp8", scale=None, out_dtype=torch.bfloat16,
                   stats: bool = False, probs: bool = False, efq: bool = False):
@@ -307,15 +384,29 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
     probs=True also the E2M1 probability blocks (p_codes, p_scales).
     efq=True: the exp-free EFQ probability rule (mx_attention_fwd_efq)."""
     f = _fmt(v_fmt)
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
-        raise MxError(4, "attention_fwd needs bf16 q and k")
-    for t in (q, k, v_codes, v_scales):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous GPU tensors")
+    if f not in _V_FORMATS:
+        raise MxError(4, f"V format {v_fmt}")
+    for t, nm in ((q, "q"), (k, "k")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError(f"{nm} must be a [heads, len, d] tensor")
+        if t.dtype != torch.bfloat16:
+            raise MxError(4, "attention_fwd needs bf16 q and k")
     heads, lq, d = q.shape
     lk = k.shape[1]
     if k.shape != (heads, lk, d):
         raise ValueError("k must be [heads, lk, d] with q's heads and d")
+    if lk % BLOCK:
+        raise ValueError(f"lk ({lk}) must be a multiple of {BLOCK}")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise MxError(4, f"dtype {out_dtype}")
+    _need(q, "q", torch.bfloat16, heads * lq * d * 2)
+    _need(k, "k", torch.bfloat16, heads * lk * d * 2)
+    nbv = heads * d * (lk // BLOCK)
+    _need(v_codes, "v_codes", torch.uint8, nbv * BYTES_PER_BLOCK[f])
+    _need(v_scales, "v_scales", torch.uint8, nbv)
+    _on_gpu(q, "q")
+    for t, nm in ((k, "k"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _on_gpu(t, nm, q)
     if scale is None:
         scale = d ** -0.5
     o = torch.empty((heads, lq, d), dtype=out_dtype, device=q.device)

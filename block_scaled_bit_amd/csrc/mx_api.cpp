@@ -80,8 +80,8 @@ extern "C" {
 
 int mx_abi_version(void) { return MX_ABI_VERSION; }
 
-const char* mx_status_str(int status) {
-  switch (status) {
+const char* mx_status_str(mx_status status) {
+  switch ((int)status) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "a required pointer is NULL";
     case MX_ERR_SHAPE: return "bad shape: rows/cols must be >= 0 and cols a multiple of 32";

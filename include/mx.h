@@ -106,8 +106,9 @@ typedef enum {
 /* MX_ABI_VERSION of the built library. */
 int mx_abi_version(void);
 
-/* Static description of a status; never NULL. */
-const char *mx_status_str(int status);
+/* Static description of a status; never NULL (an unknown value gives
+ * "unknown status"). */
+const char *mx_status_str(mx_status status);
 
 /* Sizes in bytes of the codes, scales and aux buffers for a [rows, cols]
  * tensor (aux is 0 except for AXS-6).  Any output pointer may be NULL. */
@@ -146,7 +147,17 @@ mx_status mx_quantize_batch(mx_format fmt, int block, mx_dtype in_dtype,
                             const mx_tensor_desc *tensors, int count,
                             void *stream);
 
-/* Dequantize: codes + scales (+ aux) -> y [rows, cols] of out_dtype. */
+/* Dequantize: codes + scales (+ aux) -> y [rows, cols] of out_dtype, the
+ * inverse of mx_quantize ("Online MXFP6", "Start a model": the stored form
+ * is the packed codes plus one E8M0 scale per 32 values, from which the
+ * values are rebuilt; "EFQ-Softmax" explainer, article: the quantized
+ * operand is what feeds both the PV product and the denominator, so its
+ * decoded values are the ones the method computes with).  Each value is
+ * sign * value(code) * 2^(byte - 127), rounded to out_dtype; NaN cases as
+ * under "dequantize" above.  codes, scales and aux are laid out as
+ * mx_quantize writes them (aux: AXS-6 only, else ignored and may be NULL);
+ * y must be 16-byte aligned and must not overlap the inputs.  Errors as
+ * for mx_quantize. */
 mx_status mx_dequantize(mx_format fmt, int block, const void *codes,
                         const uint8_t *scales, const uint8_t *aux,
                         int64_t rows, int64_t cols, mx_dtype out_dtype,

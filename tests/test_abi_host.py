@@ -135,6 +135,64 @@ def test_python_helpers_reject_host_tensors(mx):
     assert mx.FORMATS["mxfp6"] == mx.MX_FP6_E2M3 and mx.FORMATS["mxfp8"] == mx.MX_FP8_E4M3
 
 
+def test_python_helpers_check_every_buffer_before_launching(mx):
+    """Each helper refuses a buffer of the wrong dtype, byte size, layout or
+    device with ValueError before anything reaches the C ABI; the size and
+    layout checks come first, so host tensors exercise them here."""
+    import torch
+    u8 = torch.uint8
+    nb = 4 * 2  # a [4, 64] tensor: 8 blocks
+    good_codes, good_scales = torch.zeros(4, 2, 24, dtype=u8), torch.zeros(4, 2, dtype=u8)
+
+    def bad(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    # dequantize: codes must hold nb * bytes-per-block bytes of uint8
+    bad(mx.dequantize, torch.zeros(4, 2, 16, dtype=u8), good_scales, fmt="mxfp6", match="codes holds")
+    bad(mx.dequantize, torch.zeros(4, 2, 24, dtype=u8), good_scales, fmt="mxfp4", match="codes holds")
+    bad(mx.dequantize, torch.zeros(4, 2, 12, dtype=torch.int16), good_scales, match="codes must be")
+    bad(mx.dequantize, torch.zeros(4, 2, 48, dtype=u8)[..., ::2], good_scales, match="contiguous")
+    bad(mx.dequantize, good_codes, torch.zeros(4, 2, dtype=torch.int32), match="scales must be")
+    bad(mx.dequantize, good_codes, good_scales, fmt="e3m3", match="codes holds")  # 28 B per block
+    # AXS-6 also needs its config plane of ceil(nb / 4) bytes
+    bad(mx.dequantize, good_codes, good_scales, None, "axs6", match="aux must be a torch tensor")
+    bad(mx.dequantize, good_codes, good_scales, torch.zeros(nb, dtype=u8), "axs6", match="aux holds")
+    # well-formed host buffers fail only on the device check
+    bad(mx.dequantize, good_codes, good_scales, match="GPU memory")
+    bad(mx.dequantize, good_codes, good_scales, torch.zeros(2, dtype=u8), "axs6", match="GPU memory")
+    with pytest.raises(mx.MxError):
+        mx.dequantize(good_codes, good_scales, fmt="mxfp6", block=16)
+
+    # fake_quantize: out must match x's shape and dtype exactly
+    x = torch.zeros(4, 64)
+    bad(mx.fake_quantize, x, out=torch.zeros(4, 64, dtype=torch.bfloat16), match="out must be")
+    bad(mx.fake_quantize, x, out=torch.zeros(4, 32), match="shape")
+    bad(mx.fake_quantize, x, out=torch.zeros(64, 4).t(), match="contiguous")
+    bad(mx.fake_quantize, x, out=torch.zeros(4, 64), match="GPU memory")
+    bad(mx.fake_quantize, torch.zeros(4, 48), match="multiple of 32")
+    bad(mx.quantize, torch.zeros(8, 64)[:, :32], match="contiguous")
+    bad(mx.quantize_many, [torch.zeros(4, 64), torch.zeros(4, 40)], match="multiple of 32")
+
+    # attention_fwd: V's codes and scales must match (heads, 128, lk/32) of
+    # the V format
+    q = torch.zeros(2, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 96, 128, dtype=torch.bfloat16)
+    vc = torch.zeros(2, 128, 3, 32, dtype=u8)
+    vs = torch.zeros(2, 128, 3, dtype=u8)
+    bad(mx.attention_fwd, q, k, vc, vs, "mxfp6", match="v_codes holds")
+    bad(mx.attention_fwd, q, k, vc[:, :, :2].contiguous(), vs, "mxfp8", match="v_codes holds")
+    bad(mx.attention_fwd, q, k, vc, vs[:, :, :2].contiguous(), "mxfp8", match="v_scales holds")
+    bad(mx.attention_fwd, q, k[:, :80].contiguous(), vc, vs, "mxfp8", match="multiple of 32")
+    bad(mx.attention_fwd, q, torch.zeros(3, 96, 128, dtype=torch.bfloat16), vc, vs, match="k must be")
+    bad(mx.attention_fwd, q, k, vc.to(torch.int16), vs, "mxfp8", match="v_codes must be")
+    bad(mx.attention_fwd, q, k, vc, vs, "mxfp8", match="GPU memory")
+    with pytest.raises(mx.MxError):
+        mx.attention_fwd(q, k, vc, vs, "axs6")
+    with pytest.raises(mx.MxError):
+        mx.attention_fwd(q.float(), k, vc, vs, "mxfp8")
+
+
 def test_generic_exmy_formats_host_checks(mx):
     assert mx.mx_buffer_sizes(mx.MX_EXMY(3, 3), 32, 4, 64) == (4 * 2 * 28, 8, 0)
     assert mx.mx_buffer_sizes("e0m8", 32, 1, 32) == (36, 1, 0)

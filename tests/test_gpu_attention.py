@@ -28,7 +28,7 @@ import torch
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 from gpu_util import to_dev, to_host
 
 pytestmark = pytest.mark.gpu

@@ -5,7 +5,7 @@ import torch
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 from gpu_util import assert_bytes_equal, to_dev, to_host
 
 pytestmark = pytest.mark.gpu

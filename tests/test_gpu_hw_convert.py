@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import brute
-from block_scaled_bit_amd import workloads
+import workloads
 
 pytestmark = pytest.mark.gpu
 

@@ -22,7 +22,7 @@ import pytest
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 
 E2M1, E4M3 = oracle.FP4_E2M1, oracle.FP8_E4M3
 V_FORMATS = [oracle.FP8_E4M3, oracle.FP6_E2M3, oracle.FP6_E3M2, oracle.FP4_E2M1]

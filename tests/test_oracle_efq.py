@@ -17,7 +17,7 @@ import pytest
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 
 E2M1 = oracle.FP4_E2M1
 G = brute.grid(E2M1)            # magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6

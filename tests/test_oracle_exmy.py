@@ -12,7 +12,7 @@ import torch
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 
 EXMY = oracle.EXMY_FORMATS
 ids = [f"e{(f >> 4) & 15}m{f & 15}" for f in EXMY]

@@ -14,7 +14,7 @@ from hypothesis import strategies as st
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 
 MX = [oracle.FP6_E2M3, oracle.FP6_E3M2, oracle.FP4_E2M1, oracle.FP8_E4M3, oracle.AXS6]
 EXMY = oracle.EXMY_FORMATS

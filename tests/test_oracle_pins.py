@@ -15,7 +15,7 @@ import torch
 
 import brute
 import oracle
-from block_scaled_bit_amd import workloads
+import workloads
 
 FMTS = [oracle.FP6_E2M3, oracle.FP6_E3M2, oracle.FP4_E2M1, oracle.FP8_E4M3, oracle.AXS6]
 MX_FMTS = FMTS[:4]
