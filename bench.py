@@ -10,15 +10,18 @@ cache when it is reused, and everything is resident in HBM before timing.
 Prints ONE JSON line.  value = GB/s of bf16 input consumed (1 GB = 1e9 B);
 roofline.achieved = algorithmic bytes (input + codes + scales) per launch over
 the measured average launch time, against the 8 TB/s HBM peak.  The other
-steps of the path (E3M2, dequantize, AXS-6 fake-quantize, exp-then-quantize
-probabilities, dynamic activations) are timed the same way and reported under
-"secondary".  cpu_baseline times the CPU oracle on a bounded row sample of the
-same input, and the same rows are compared byte for byte with the GPU output.
+steps of the path (E3M2, dequantize, eXmY, AXS-6, exp-then-quantize
+probabilities, dynamic activations, the fused attention forward, the layer
+conversion, the small fp32 tensor) are timed the same way and reported under
+"secondary".  The cpu_baseline leg runs the CPU oracle on the host's cores:
+it times the headline op (T threads over the whole input, one thread over a
+row sample), and compares every op's full output with the GPU's byte for
+byte, recording the oracle's rate beside each; any difference makes the run
+exit with status 1 after printing its line.
 """
 from __future__ import annotations
 
 import argparse
-import concurrent.futures as cf
 import hashlib
 import json
 import os
@@ -119,10 +122,10 @@ def headline(mx, x_np, steps, warmup):
         if st:
             raise mx.MxError(st, "mx_quantize")
 
-    ms = time_launches(step, nsets, steps, warmup)
+    ms = time_launches(step, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
 
-    # the same HBM, same rotation: a plain device-to-device copy of the input
-    # (reads and writes in_bytes each) as a measured streaming ceiling
+    # the same HBM, same rotation: torch's device-to-device copy of the input
+    # (reads and writes in_bytes each), a reference rate, not a ceiling
     def copy(i):
         xs[(i + 1) % nsets].copy_(xs[i])
 
@@ -139,7 +142,7 @@ def headline(mx, x_np, steps, warmup):
             if probe(xs[i].data_ptr(), nb, codes[i].data_ptr(), scales[i].data_ptr(), stream):
                 raise RuntimeError("probe_mix_copy launch failed")
 
-        ms_mix = time_launches(mix, nsets, steps, warmup)
+        ms_mix = time_launches(mix, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
         # the probe wrote its own bytes into the output buffers: set 0 gets
         # the quantizer's output back for the parity check against the oracle
         step(0)
@@ -179,118 +182,248 @@ def mix_copy_probe():
     return fn
 
 
-def secondary(mx, steps):
-    """Other steps of the path, each at its workload's full size."""
+def host(t):
+    """Device tensor -> numpy (bf16 as uint16 bit patterns)."""
     import numpy as np
     import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class Secondary:
+    """The other steps of the path, each at its workload's full size: timed
+    like the headline, then compared byte for byte with the oracle over the
+    whole tensor (row ranges on the host's cores), with the oracle's own
+    rate recorded beside the GPU's."""
+
+    def __init__(self, mx, steps, threads):
+        import torch
+        self.mx, self.torch = mx, torch
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.k = max(10, steps // 4)
+        self.threads = threads
+        self.res = {}
+        self.failed = []
+
+    def launch(self, name, fn):
+        """fn(i) -> mx status; a nonzero status raises instead of being timed."""
+        mx = self.mx
+
+        def call(i):
+            st = fn(i)
+            if st:
+                raise mx.MxError(st, name)
+        return call
+
+    def time(self, name, fn, nsets, in_b, out_b, note, steps=None, warm=3):
+        ms = time_launches(self.launch(name, fn), nsets, steps or self.k, warm,
+                           min_warm_s=SECONDARY_WARM_S)
+        self.res[name] = {"us": round(ms * 1e3, 2), "input_GBps": round(in_b / ms / 1e6, 1),
+                          "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
+                          "bytes": in_b + out_b, "workload": note}
+        return ms
+
+    def oracle(self, fn, rows):
+        """The oracle over all rows, split across the host threads; returns
+        (result, wall seconds)."""
+        import oracle
+        t = time.perf_counter()
+        out = oracle.by_rows(fn, rows, self.threads)
+        return out, time.perf_counter() - t
+
+    def parity(self, name, pairs, in_b, oracle_s, what):
+        """pairs: (gpu array, oracle array) compared byte for byte."""
+        import numpy as np
+        ok = all(np.array_equal(np.ascontiguousarray(g).reshape(-1).view(np.uint8),
+                                np.ascontiguousarray(o).reshape(-1).view(np.uint8))
+                 for g, o in pairs)
+        self.res[name]["parity"] = {"bit_exact": bool(ok), "compared": what}
+        self.res[name]["oracle_GBps"] = round(in_b / oracle_s / 1e9, 3)
+        self.res[name]["oracle_threads"] = self.threads
+        if not ok:
+            self.failed.append(name)
+
+
+def secondary(mx, steps, threads, check=True):
+    """Other steps of the path, each at its workload's full size, each
+    compared with the oracle over the whole tensor (check=False: timing
+    only, for profiling runs)."""
+    import numpy as np
+    import torch
+
+    import oracle
     import workloads
-    res = {}
-    stream = torch.cuda.current_stream().cuda_stream
-    k = max(10, steps // 4)
+    S = Secondary(mx, steps, threads)
+    st = S.stream
+    BF, FP = mx.MX_BF16, mx.MX_FP32
 
-    def record(name, ms, in_b, out_b, note):
-        res[name] = {"us": round(ms * 1e3, 2), "input_GBps": round(in_b / ms / 1e6, 1),
-                     "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
-                     "bytes": in_b + out_b, "workload": note}
-
-    # linear weight: E3M2 quantize, E2M3 and E3M2 dequantize to bf16
+    # -- linear weight: E3M2 quantize, E2M3 / E3M2 dequantize to bf16, and
+    #    the generic 7-bit e3m3 quantize and dequantize
     w = workloads.linear_weight()
     rows, cols = w.shape
     nb = rows * cols // 32
-    n = rotation_sets(rows * cols * 2 + nb * 25)
+    note = "linear_weight bf16 14336x4096"
+    n = rotation_sets(rows * cols * 4 + nb * 25)
     xs = bf16_dev(w, n)
-    cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    for f, nm in ((1, "e3m2"), (0, "e2m3")):
-        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3,
-                           min_warm_s=SECONDARY_WARM_S)
-        if f == 1:
-            record("quantize_e3m2", ms, rows * cols * 2, nb * 25, "linear_weight bf16 14336x4096")
-        ms = time_launches(lambda i: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
-                           min_warm_s=SECONDARY_WARM_S)
-        record(f"dequantize_{nm}_to_bf16", ms, nb * 25, rows * cols * 2, "linear_weight bf16 14336x4096")
-    # a generic eXmY format (7-bit e3m3, 28 B per block; rounding in fp32)
-    g = mx.MX_EXMY(3, 3)
-    cg = [torch.empty(nb * 28, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_quantize(g, 32, 0, xs[i], rows, cols, cg[i], ss[i], None, stream), n, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("quantize_exmy_e3m3", ms, rows * cols * 2, nb * 29, "linear_weight bf16 14336x4096")
-    ms = time_launches(lambda i: mx.mx_dequantize(g, 32, cg[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("dequantize_exmy_e3m3_to_bf16", ms, nb * 29, rows * cols * 2, "linear_weight bf16 14336x4096")
-    del xs, cs, ss, cg
+    for f, nm, bpb in ((1, "e3m2", 24), (0, "e2m3", 24), (mx.MX_EXMY(3, 3), "exmy_e3m3", 28)):
+        cs = [torch.empty(nb * bpb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        q = lambda i, f=f, cs=cs: mx.mx_quantize(f, 32, BF, xs[i], rows, cols, cs[i], ss[i], None, st)
+        dq = lambda i, f=f, cs=cs: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, BF, ys[i], st)
+        if f != 0:  # the E2M3 quantize is the headline
+            S.time(f"quantize_{nm}", q, n, rows * cols * 2, nb * (bpb + 1), note)
+        S.launch(nm, q)(0)
+        S.time(f"dequantize_{nm}_to_bf16", dq, n, nb * (bpb + 1), rows * cols * 2, note)
+        S.launch(nm, dq)(0)
+        torch.cuda.synchronize()
+        if check:
+            gc, gs, gy = host(cs[0]), host(ss[0]), host(ys[0])
+            (oc, os_, _), t_q = S.oracle(lambda a, b, f=f: oracle.quantize(f, w[a:b]), rows)
+            oy, t_dq = S.oracle(lambda a, b, f=f: oracle.dequantize(
+                f, oc[a:b], os_[a:b], None, b - a, cols, oracle.BF16), rows)
+            if f != 0:
+                S.parity(f"quantize_{nm}", [(gc, oc), (gs, os_)], rows * cols * 2, t_q,
+                         "all 14336 rows: codes, scales")
+            S.parity(f"dequantize_{nm}_to_bf16", [(gy, oy)], nb * (bpb + 1), t_dq,
+                     "all 14336 rows: bf16 output")
+            del oc, os_, oy, gc, gs, gy
+        del cs
+    del xs, ys, ss, w
 
-    # AXS-6 weight: fake-quantize and quantize
+    # -- AXS-6 weight: fake-quantize and quantize (+ config plane); bits per
+    #    value and each block's largest error
     a = workloads.axs6_weight()
     rows, cols = a.shape
     nb = rows * cols // 32
+    note = "axs6_weight bf16 4096x4096"
     n = rotation_sets(rows * cols * 4)
     xs = bf16_dev(a, n)
     ys = [torch.empty_like(xs[0]) for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_fake_quantize(4, 32, 0, xs[i], ys[i], rows, cols, stream), n, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("fake_quantize_axs6", ms, rows * cols * 2, rows * cols * 2, "axs6_weight bf16 4096x4096")
+    fq = lambda i: mx.mx_fake_quantize(4, 32, BF, xs[i], ys[i], rows, cols, st)
+    S.time("fake_quantize_axs6", fq, n, rows * cols * 2, rows * cols * 2, note)
     cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     aa = [torch.empty((nb + 3) // 4, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    ms = time_launches(lambda i: mx.mx_quantize(4, 32, 0, xs[i], rows, cols, cs[i], ss[i], aa[i], stream), n, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("quantize_axs6", ms, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, "axs6_weight bf16 4096x4096")
-    del xs, ys, cs, ss, aa
+    q = lambda i: mx.mx_quantize(4, 32, BF, xs[i], rows, cols, cs[i], ss[i], aa[i], st)
+    S.time("quantize_axs6", q, n, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, note)
+    S.launch("fq", fq)(0)
+    S.launch("q", q)(0)
+    torch.cuda.synchronize()
+    gy, gc, gs, ga = host(ys[0]), host(cs[0]), host(ss[0]), host(aa[0])
+    if check:
+        oy, t_fq = S.oracle(lambda r0, r1: oracle.fake_quantize(4, a[r0:r1]), rows)
+        (oc, os_, oa), t_q = S.oracle(lambda r0, r1: oracle.quantize(4, a[r0:r1]), rows)
+        S.parity("fake_quantize_axs6", [(gy, oy)], rows * cols * 2, t_fq,
+                 "all 4096 rows: bf16 output")
+        S.parity("quantize_axs6", [(gc, oc), (gs, os_), (ga, oa)], rows * cols * 2, t_q,
+                 "all 4096 rows: codes, shared exponents, config plane")
+    # bits per value from the buffers; per-block error against the grid's
+    # bound: half a step 2^(E-5) below the top value, 2^(E-4) where the
+    # block maximum saturates at 31/16 2^E (E = byte - 127)
+    S.res["quantize_axs6"]["bits_per_value"] = 8 * (gc.size + gs.size + ga.size) / (rows * cols)
+    xf = workloads.bf16_bits_to_f32(a).astype(np.float64).reshape(nb, 32)
+    yf = workloads.bf16_bits_to_f32(gy).astype(np.float64).reshape(nb, 32)
+    err = np.abs(xf - yf)
+    blk = err.max(axis=1)
+    E = gs.reshape(-1).astype(np.float64) - 127
+    top = (31.0 / 16.0) * np.exp2(E)[:, None]
+    bound = np.where(np.abs(xf) > top, np.exp2(E - 4)[:, None], np.exp2(E - 5)[:, None])
+    S.res["fake_quantize_axs6"]["block_max_abs_err"] = {
+        "max": float(blk.max()), "mean": float(blk.mean()),
+        "max_over_half_step": float((blk / np.exp2(E - 5)).max()),
+        "bound_ok": bool(np.all(err <= bound)),
+        "note": "per 32-value block: max |x - fq(x)|; bound 2^(E-5), 2^(E-4) for values above "
+                "31/16 2^E"}
+    del xs, ys, cs, ss, aa, a, xf, yf, err, bound
 
-    # dynamic activations: E4M3 and E2M3 quantize, E4M3 dequantize
+    # -- dynamic activations: E4M3 and E2M3 quantize and dequantize
     act = workloads.activations()
     rows, cols = act.shape
     nb = rows * cols // 32
-    n = rotation_sets(rows * cols * 2 + nb * 33)
+    note = "activations bf16 16384x8192"
+    n = rotation_sets(rows * cols * 4 + nb * 33)
     xs = bf16_dev(act, n)
-    cs = [torch.empty(nb * 32, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     for f, nm, bpb in ((3, "e4m3", 32), (0, "e2m3", 24)):
-        ms = time_launches(lambda i: mx.mx_quantize(f, 32, 0, xs[i], rows, cols, cs[i], ss[i], None, stream), n, k, 3,
-                           min_warm_s=SECONDARY_WARM_S)
-        record(f"quantize_{nm}_activations", ms, rows * cols * 2, nb * (bpb + 1), "activations bf16 16384x8192")
-    ms = time_launches(lambda i: mx.mx_dequantize(3, 32, cs[i], ss[i], None, rows, cols, 0, xs[i], stream), n, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("dequantize_e4m3_activations", ms, nb * 33, rows * cols * 2, "activations bf16 16384x8192")
-    del xs, cs, ss
+        cs = [torch.empty(nb * bpb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        q = lambda i, f=f, cs=cs: mx.mx_quantize(f, 32, BF, xs[i], rows, cols, cs[i], ss[i], None, st)
+        dq = lambda i, f=f, cs=cs: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, BF, ys[i], st)
+        S.time(f"quantize_{nm}_activations", q, n, rows * cols * 2, nb * (bpb + 1), note)
+        S.launch(nm, q)(0)
+        S.time(f"dequantize_{nm}_activations", dq, n, nb * (bpb + 1), rows * cols * 2, note)
+        S.launch(nm, dq)(0)
+        torch.cuda.synchronize()
+        gs = host(ss[0])
+        S.res[f"quantize_{nm}_activations"]["poisoned_blocks"] = int((gs == 0xFF).sum())
+        if check:
+            gc, gy = host(cs[0]), host(ys[0])
+            (oc, os_, _), t_q = S.oracle(lambda a, b, f=f: oracle.quantize(f, act[a:b]), rows)
+            oy, t_dq = S.oracle(lambda a, b, f=f: oracle.dequantize(
+                f, oc[a:b], os_[a:b], None, b - a, cols, oracle.BF16), rows)
+            S.parity(f"quantize_{nm}_activations", [(gc, oc), (gs, os_)], rows * cols * 2, t_q,
+                     "all 16384 rows: codes, scales")
+            S.parity(f"dequantize_{nm}_activations", [(gy, oy)], nb * (bpb + 1), t_dq,
+                     "all 16384 rows: bf16 output")
+            del gc, gy, oc, os_, oy
+        del cs, gs
+    del xs, ys, ss, act
 
-    # attention probabilities: exp-then-quantize to E2M1 (2 GiB of scores)
+    # -- attention probabilities: exp-then-quantize to E2M1 (2 GiB of
+    #    scores), then the dequantized P
     s = workloads.attn_scores()
     rows, cols = s.shape
     nb = rows * cols // 32
+    note = "attn_scores fp32 32x4096x4096"
     sd = torch.from_numpy(s).cuda()
-    del s
     c = torch.empty(nb * 16, dtype=torch.uint8, device="cuda")
     sc = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    ms = time_launches(lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream), 1, max(5, k // 4), 2,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("softmax_quantize_e2m1", ms, rows * cols * 4, nb * 17, "attn_scores fp32 32x4096x4096")
+    pd = torch.empty_like(sd)
+    kk = max(5, S.k // 4)
+    sq = lambda i: mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, st)
+    S.time("softmax_quantize_e2m1", sq, 1, rows * cols * 4, nb * 17, note, steps=kk, warm=2)
     # its floor: the same grid, loads and stores with the arithmetic folded
-    # away (tests/hwprobe/bw_probe.hip), then the real outputs again
+    # away (tests/hwprobe/bw_probe.hip)
     floor = rows_floor_probe()
     if floor is not None:
         def fl(i):
-            if floor(sd.data_ptr(), rows, cols, c.data_ptr(), sc.data_ptr(), stream):
-                raise RuntimeError("probe_rows_floor launch failed")
+            return floor(sd.data_ptr(), rows, cols, c.data_ptr(), sc.data_ptr(), st)
 
-        ms_floor = time_launches(fl, 1, max(5, k // 4), 2, min_warm_s=SECONDARY_WARM_S)
-        res["softmax_quantize_e2m1"].update(
-            floor_us=round(ms_floor * 1e3, 2), frac_of_floor=round(ms_floor / ms, 4),
-            floor_note="same grid, loads and stores with no exp or conversion")
-        mx.mx_softmax_quantize(2, 32, sd, rows, cols, c, sc, stream)
-    ms = time_launches(lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, 1, sd, stream), 1, max(5, k // 4), 2,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("dequantize_e2m1_to_fp32", ms, nb * 17, rows * cols * 4, "attn_scores fp32 32x4096x4096")
-    del sd, c, sc
+        ms_floor = time_launches(S.launch("probe_rows_floor", fl), 1, kk, 2,
+                                 min_warm_s=SECONDARY_WARM_S)
+        r = S.res["softmax_quantize_e2m1"]
+        r.update(floor_us=round(ms_floor * 1e3, 2), frac_of_floor=round(ms_floor * 1e3 / r["us"], 4),
+                 floor_note="same grid, loads and stores with no exp or conversion")
+    S.launch("sq", sq)(0)  # the real outputs again, after the floor probe
+    dq = lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, FP, pd, st)
+    S.time("dequantize_e2m1_to_fp32", dq, 1, nb * 17, rows * cols * 4, note, steps=kk, warm=2)
+    torch.cuda.synchronize()
+    if check:
+        gc, gs, gp = host(c), host(sc), host(pd)
+        del sd, pd, c, sc
+        (oc, os_), t_q = S.oracle(lambda a, b: oracle.softmax_quantize(2, s[a:b]), rows)
+        op, t_dq = S.oracle(lambda a, b: oracle.dequantize(2, oc[a:b], os_[a:b], None, b - a,
+                                                           cols, oracle.FP32), rows)
+        S.parity("softmax_quantize_e2m1", [(gc, oc), (gs, os_)], rows * cols * 4, t_q,
+                 "all 131072 rows: codes, scales")
+        S.parity("dequantize_e2m1_to_fp32", [(gp, op)], nb * 17, t_dq,
+                 "all 131072 rows: fp32 P")
+        del gc, gs, gp, oc, os_, op
+    else:
+        del sd, pd, c, sc
+    del s
 
-    # the same scores inside a fused attention forward: 32 heads x 4096
-    # queries x 4096 keys, d = 128, bf16 q/k, V^T in MXFP8, bf16 output
-    res.update(attention_line(mx, k))
+    # -- the same scores inside a fused attention forward: 32 heads x 4096
+    #    queries x 4096 keys, d = 128, bf16 q/k, V^T in MXFP8, bf16 output
+    S.res.update(attention_line(mx, S.k))
 
-    # layer-by-layer conversion of a synthetic dense decoder (4 layers,
-    # hidden 4096, MLP 14336, 1024-wide k/v): weights already on the GPU, and
-    # again from pinned host memory (that rate includes the PCIe upload)
+    # -- layer-by-layer conversion of a synthetic dense decoder (4 layers,
+    #    hidden 4096, MLP 14336, 1024-wide k/v): weights already on the
+    #    GPU, and again from pinned host memory (that rate includes the PCIe
+    #    upload)
     from block_scaled_bit_amd import convert
     g = torch.Generator(device="cuda").manual_seed(11)
     shapes = {"self_attn.q_proj": (4096, 4096), "self_attn.k_proj": (1024, 4096),
@@ -302,6 +435,7 @@ def secondary(mx, steps):
     cfg = convert.QuantConfig.from_options("mxfp6")
     in_b = sum(t.numel() * 2 for t in model.values())
     out_b = sum(t.numel() // 32 * 25 for t in model.values())
+    note = "synthetic decoder, 4 layers x 7 weights, hidden 4096, MLP 14336 (mxfp6 shorthand)"
     for src_name, src in (("device", model), ("pinned_host", None)):
         if src is None:
             src = {k: v.cpu().pin_memory() for k, v in model.items()}
@@ -315,20 +449,54 @@ def secondary(mx, steps):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        record(f"convert_dense_4_layers_from_{src_name}", ms, in_b, out_b,
-               "synthetic decoder, 4 layers x 7 weights, hidden 4096, MLP 14336 (mxfp6 shorthand)")
+        name = f"convert_dense_4_layers_from_{src_name}"
+        S.res[name] = {"us": round(ms * 1e3, 2), "input_GBps": round(in_b / ms / 1e6, 1),
+                       "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
+                       "bytes": in_b + out_b, "workload": note}
+        if src_name == "device" and check:
+            # every converted tensor against the oracle
+            pairs, t_or = [], 0.0
+            for nm_, t in model.items():
+                wq = out[nm_]
+                xh = host(t)
+                (oc, os_, _), dt = S.oracle(lambda a, b, xh=xh: oracle.quantize(0, xh[a:b]),
+                                            xh.shape[0])
+                t_or += dt
+                pairs += [(host(wq.codes), oc), (host(wq.scales), os_)]
+            S.parity(name, pairs, in_b, t_or, "all 28 tensors: codes, scales")
         del out
     del model, src
 
-    # small fp32 tensor: latency of the three ops
-    xsm = torch.from_numpy(workloads.weights_small()).cuda()
+    # -- small fp32 tensor: the three ops (launch-bound)
+    x = workloads.weights_small()
+    xsm = torch.from_numpy(x).cuda()
     cc = torch.empty(1024 * 24, dtype=torch.uint8, device="cuda")
     s1 = torch.empty(1024, dtype=torch.uint8, device="cuda")
-    yy = torch.empty_like(xsm)
-    ms = time_launches(lambda i: mx.mx_quantize(0, 32, 1, xsm, 128, 256, cc, s1, None, stream), 1, k, 3,
-                       min_warm_s=SECONDARY_WARM_S)
-    record("quantize_e2m3_weights_small", ms, 131072, 25600, "weights_small fp32 128x256 (launch-bound)")
-    return res
+    yq = torch.empty_like(xsm)
+    yf = torch.empty_like(xsm)
+    note = "weights_small fp32 128x256 (launch-bound)"
+    q = lambda i: mx.mx_quantize(0, 32, FP, xsm, 128, 256, cc, s1, None, st)
+    dq = lambda i: mx.mx_dequantize(0, 32, cc, s1, None, 128, 256, FP, yq, st)
+    fq = lambda i: mx.mx_fake_quantize(0, 32, FP, xsm, yf, 128, 256, st)
+    S.time("quantize_e2m3_weights_small", q, 1, 131072, 25600, note)
+    S.time("dequantize_e2m3_weights_small", dq, 1, 25600, 131072, note)
+    S.time("fake_quantize_e2m3_weights_small", fq, 1, 131072, 131072, note)
+    for f_ in (q, dq, fq):
+        S.launch("small", f_)(0)
+    torch.cuda.synchronize()
+    if not check:
+        return S.res, S.failed
+    (oc, os_, _), t_q = S.oracle(lambda a, b: oracle.quantize(0, x[a:b]), 128)
+    oy, t_dq = S.oracle(lambda a, b: oracle.dequantize(0, oc[a:b], os_[a:b], None, b - a, 256,
+                                                       oracle.FP32), 128)
+    of, t_fq = S.oracle(lambda a, b: oracle.fake_quantize(0, x[a:b]), 128)
+    S.parity("quantize_e2m3_weights_small", [(host(cc), oc), (host(s1), os_)], 131072, t_q,
+             "all 128 rows: codes, scales")
+    S.parity("dequantize_e2m3_weights_small", [(host(yq), oy)], 25600, t_dq,
+             "all 128 rows: fp32 output")
+    S.parity("fake_quantize_e2m3_weights_small", [(host(yf), of)], 131072, t_fq,
+             "all 128 rows: fp32 output")
+    return S.res, S.failed
 
 
 def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
@@ -370,34 +538,53 @@ def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
     return out
 
 
-def cpu_baseline(x_np, gpu_codes, gpu_scales, passes=3):
-    """The CPU oracle, as it stands, on the same input: T threads, each on one
-    contiguous range of rows (blocks never cross rows); the minimum of
-    `passes` full passes.  The oracle's output is compared with the GPU's."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x_np, gpu_codes, gpu_scales, threads, passes=3, single_rows=2048):
+    """The CPU oracle, as it stands, on the headline's input: T threads, each
+    on one contiguous range of rows (blocks never cross rows), over the whole
+    tensor, and one thread on its first `single_rows` rows; the minimum of
+    `passes` passes each.  The T-thread output is compared with the GPU's."""
     import numpy as np
 
     import oracle
     rows, cols = x_np.shape
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    bounds = [(rows * i) // threads for i in range(threads + 1)]
-    best, parts = None, None
+    best, out = None, None
     for _ in range(passes):
         t = time.perf_counter()
-        with cf.ThreadPoolExecutor(threads) as ex:
-            parts = list(ex.map(lambda i: oracle.quantize(0, x_np[bounds[i]:bounds[i + 1]]),
-                                range(threads)))
+        out = oracle.by_rows(lambda a, b: oracle.quantize(0, x_np[a:b])[:2], rows, threads)
         wall = time.perf_counter() - t
         best = wall if best is None else min(best, wall)
-    oc = np.concatenate([p[0] for p in parts])
-    os_ = np.concatenate([p[1] for p in parts])
-    g_codes = gpu_codes.cpu().numpy().reshape(oc.shape)
-    g_scales = gpu_scales.cpu().numpy().reshape(os_.shape)
-    parity = bool(np.array_equal(g_codes, oc) and np.array_equal(g_scales, os_))
+    oc, os_ = out
+    parity = bool(np.array_equal(host(gpu_codes).reshape(oc.shape), oc)
+                  and np.array_equal(host(gpu_scales).reshape(os_.shape), os_))
+    sample = x_np[:single_rows]
+    best1 = None
+    for _ in range(passes):
+        t = time.perf_counter()
+        oracle.quantize(0, sample)
+        wall = time.perf_counter() - t
+        best1 = wall if best1 is None else min(best1, wall)
     value = rows * cols * 2 / best / 1e9
     base = {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole bf16 14336x4096 input ({rows * cols} values), E2M3 "
                       f"quantize+pack, {threads} threads x ~{rows // threads} rows, best of "
-                      f"{passes} passes ({best:.2f} s wall each)"}
+                      f"{passes} passes ({best:.2f} s wall each)",
+            "single_thread_GBps": round(single_rows * cols * 2 / best1 / 1e9, 4),
+            "single_thread_sample": f"rows 0..{single_rows - 1} ({single_rows * cols} values), "
+                                    f"one thread, best of {passes} ({best1:.2f} s)",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "threads_note": "T = the CPUs this process may use, at most 16 (the host CPU share "
+                            "of one GPU)"}
     return base, parity, rows
 
 
@@ -481,10 +668,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(digest)},
-        "copy_ceiling": {"d2d_copy_GBps": round(copy_gbs, 1),
-                         "frac_of_copy": round(achieved / copy_gbs, 4),
-                         "note": "device-to-device copy of the bf16 input (read + write "
-                                 "bytes / time), same buffers and rotation"},
+        "d2d_copy_reference": {"d2d_copy_GBps": round(copy_gbs, 1),
+                               "headline_over_copy": round(achieved / copy_gbs, 4),
+                               "note": "torch's device-to-device copy of the bf16 input (read + "
+                                       "write bytes / time), same buffers and rotation; a "
+                                       "reference rate, not a ceiling"},
     }
     if ms_mix is not None:
         out["mix_ceiling"] = {
@@ -493,17 +681,28 @@ def main():
             "headline_frac_of_ceiling": round(ms_mix / ms, 4),
             "note": "copy kernel with the quantizer's grid, loads and stores and no arithmetic "
                     "(tests/hwprobe/bw_probe.hip), same buffers, rotation, warm-up and steps"}
+    import oracle
+    threads = oracle.worker_threads()
+    failed = []
     if not args.no_cpu_baseline:
-        base, parity, nrows = cpu_baseline(x, codes0, scales0)
+        base, parity, nrows = cpu_baseline(x, codes0, scales0, threads)
         out["cpu_baseline"] = base
         out["parity"] = {"bit_exact": parity, "rows_compared": nrows}
+        if not parity:
+            failed.append("headline")
     if not args.no_secondary:
         del codes0, scales0
         torch.cuda.empty_cache()
-        out["secondary"] = secondary(mx, args.steps)
+        out["secondary"], bad = secondary(mx, args.steps, threads,
+                                          check=not args.no_cpu_baseline)
+        failed += bad
+        if not args.no_cpu_baseline:
+            out["parity"] = dict(out["parity"], all_rows_bit_exact=not failed,
+                                 ops_checked=1 + sum("parity" in r
+                                                     for r in out["secondary"].values()))
     print(json.dumps(out), flush=True)
-    if out.get("parity", {}).get("bit_exact") is False:
-        print("bench.py: the GPU's codes or scales differ from the oracle's", file=sys.stderr,
+    if failed:
+        print(f"bench.py: the GPU's output differs from the oracle's in {failed}", file=sys.stderr,
               flush=True)
         sys.exit(1)
 

@@ -253,3 +253,28 @@ def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,
     if rc:
         raise ValueError("oracle attention_fwd: bad arguments")
     return o, row_max, row_sum, p_codes, p_scales
+
+
+def worker_threads() -> int:
+    """Threads for a row-split oracle pass: the CPUs this process may run on,
+    at most 16 (a one-GPU host's CPU share)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def by_rows(fn, rows: int, threads: int | None = None):
+    """Run fn(r0, r1) on `threads` contiguous row ranges at once and join the
+    parts: fn returns a tuple of arrays whose leading axis is the rows r0..r1
+    (1-D arrays, such as an AXS-6 config plane, are joined end to end; for
+    that plane every range must start at a multiple of 4 blocks).  The
+    oracle's functions work one block at a time and blocks never cross rows,
+    so the joined result equals one call over all rows.  The C library
+    releases the interpreter lock, so the ranges run in parallel."""
+    import concurrent.futures as cf
+    threads = threads or worker_threads()
+    threads = max(1, min(threads, rows)) if rows else 1
+    bounds = [(rows * i) // threads for i in range(threads + 1)]
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda i: fn(bounds[i], bounds[i + 1]), range(threads)))
+    if not isinstance(parts[0], tuple):
+        return np.concatenate(parts)
+    return tuple(np.concatenate([p[j] for p in parts]) for j in range(len(parts[0])))

@@ -142,6 +142,23 @@ def encode(fmt: int, v: np.ndarray, byte: int) -> np.ndarray:
     return (sign << (CODE_BITS[fmt] - 1)) | mag
 
 
+def encode_sorted(fmt: int, v: np.ndarray, byte: int) -> np.ndarray:
+    """The same nearest-grid-point choice as encode(), found by bisection on
+    the sorted grid instead of an all-pairs distance table (for sweeps of
+    millions of values): the two grid points around |v|/X are the only
+    candidates; the nearer wins, an exact tie goes to the even code."""
+    v = np.asarray(v, dtype=np.float64)
+    g = finite_grid(fmt)
+    assert np.all(np.diff(g) > 0)
+    a = np.minimum(np.abs(v) / 2.0 ** (byte - 127), g[-1])
+    hi = np.minimum(np.searchsorted(g, a, side="left"), g.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    dl, dh = a - g[lo], g[hi] - a
+    mag = np.where(dh < dl, hi, np.where(dl < dh, lo, np.where(lo % 2 == 0, lo, hi)))
+    sign = np.signbit(v).astype(np.int64)
+    return (sign << (CODE_BITS[fmt] - 1)) | mag
+
+
 def pack(fmt: int, codes) -> bytes:
     """Little-endian bit stream: code k occupies bits [k*w, k*w + w)."""
     w = CODE_BITS[fmt]

@@ -217,10 +217,52 @@ def test_nan_score_poisons_its_row_only(mx, efq):
     assert np.all(np.isfinite(workloads.bf16_bits_to_f32(o[0, others])))
 
 
-def test_full_size_sampled_rows(mx):
-    """32 heads x 4096 queries x 4096 keys, d = 128 (the attention-score
-    workload), E4M3 V, bf16 output, on natural scores: sampled rows against
-    the oracle (each row depends only on its own query)."""
+ROWS_FULL = [(0, 0), (5, 1234), (17, 4095), (31, 2048), (12, 77), (31, 4095), (8, 3000),
+             (20, 511)]
+
+
+def _row_ref(fmt, q, k, vc, vs, heads, h, i, scale, efq=False):
+    """The oracle on one query row (each row depends only on its own query)."""
+    return oracle.attention_fwd(fmt, q[h:h + 1, i:i + 1], k[h:h + 1],
+                                vc.reshape(heads, -1)[h:h + 1], vs.reshape(heads, -1)[h:h + 1],
+                                scale, 64, oracle.FP32, efq=efq)
+
+
+@pytest.mark.parametrize("rule", ["exp", "efq"])
+def test_full_size_exact_scores_rows_bit_exact(mx, rule):
+    """32 heads x 4096 queries x 4096 keys, d = 128, E4M3 V, bf16 output, in
+    the launch the benchmark times, on exactly summable scores: sampled rows'
+    probability blocks, scale bytes and row maxima bit-exact against the
+    oracle, and the output inside the exact bound."""
+    heads, lq, lk = 32, 4096, 4096
+    efq = rule == "efq"
+    rng = np.random.default_rng(13)
+    qd = (torch.randint(-12, 13, (heads, lq, D), device="cuda").float() / 4).to(torch.bfloat16)
+    kd = (torch.randint(-12, 13, (heads, lk, D), device="cuda").float() / 4).to(torch.bfloat16)
+    q, k = to_host(qd), to_host(kd)
+    vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
+    scale = np.float32(D ** -0.5)
+    o, rm, rs, pc, ps = mx.attention_fwd(qd, kd, to_dev(vc), to_dev(vs), "mxfp8", scale=scale,
+                                         out_dtype=torch.bfloat16, stats=True, probs=True, efq=efq)
+    torch.cuda.synchronize()
+    vmax_all = vhat_absmax(oracle.FP8_E4M3, vc, vs, heads, lk)
+    for h, i in ROWS_FULL:
+        o_ref, rm_ref, _, pc_ref, ps_ref = _row_ref(oracle.FP8_E4M3, q, k, vc, vs, heads, h, i,
+                                                    scale, efq)
+        assert np.array_equal(to_host(pc[h, i]), pc_ref[0, 0]), (h, i)
+        assert np.array_equal(to_host(ps[h, i]), ps_ref[0, 0]), (h, i)
+        assert float(rm[h, i]) == float(rm_ref[0, 0]), (h, i)
+        ref = o_ref[0, 0].astype(np.float64)
+        got = workloads.bf16_bits_to_f32(to_host(o[h, i])).astype(np.float64)
+        bound = out_bound(oracle.FP8_E4M3, lk, vmax_all[h:h + 1], ref[None, None, :], True)[0, 0]
+        assert np.all(np.abs(got - ref) <= bound), (h, i, float((np.abs(got - ref) / bound).max()))
+
+
+def test_full_size_natural_scores_rows(mx):
+    """The benchmark's workload (bf16 N(0, 1) q and k, E4M3 V, bf16 output)
+    on sampled rows: nearly every probability block equal to the oracle's,
+    and the output inside the bound derived from the two sets of
+    probability codes (as on the small natural-score inputs)."""
     heads, lq, lk = 32, 4096, 4096
     rng = np.random.default_rng(11)
     qd = torch.randn(heads, lq, D, device="cuda", dtype=torch.float32).to(torch.bfloat16)
@@ -228,18 +270,32 @@ def test_full_size_sampled_rows(mx):
     q, k = to_host(qd), to_host(kd)
     vc, vs = v_input(rng, heads, lk, oracle.FP8_E4M3)
     scale = np.float32(D ** -0.5)
-    o, rm, rs = mx.attention_fwd(qd, kd, to_dev(vc), to_dev(vs), "mxfp8", scale=scale,
-                                 out_dtype=torch.bfloat16, stats=True)
-    o, rm, rs = to_host(o), to_host(rm), to_host(rs)
+    o, rm, rs, pc, ps = mx.attention_fwd(qd, kd, to_dev(vc), to_dev(vs), "mxfp8", scale=scale,
+                                         out_dtype=torch.bfloat16, stats=True, probs=True)
+    torch.cuda.synchronize()
     vmax_all = vhat_absmax(oracle.FP8_E4M3, vc, vs, heads, lk)
-    for h, i in [(0, 0), (5, 1234), (17, 4095), (31, 2048), (12, 77)]:
-        o_ref, rm_ref, rs_ref, _, _ = oracle.attention_fwd(
-            oracle.FP8_E4M3, q[h:h + 1, i:i + 1], k[h:h + 1], vc.reshape(heads, -1)[h:h + 1],
-            vs.reshape(heads, -1)[h:h + 1], scale, 64, oracle.FP32)
+    g = brute.grid(oracle.FP4_E2M1)
+
+    def decode(pcodes, pscales):
+        nib = np.stack([pcodes & 15, pcodes >> 4], -1).reshape(pcodes.shape[:-1] + (32,))
+        return g[nib & 7] * np.exp2(pscales.astype(np.float64) - 127)[..., None]
+
+    same, total = 0, 0
+    for h, i in ROWS_FULL:
+        o_ref, rm_ref, rs_ref, pc_ref, ps_ref = _row_ref(oracle.FP8_E4M3, q, k, vc, vs, heads, h,
+                                                         i, scale)
+        gpc, gps = to_host(pc[h, i]), to_host(ps[h, i])
+        same += int((np.all(gpc == pc_ref[0, 0], axis=-1) & (gps == ps_ref[0, 0])).sum())
+        total += gps.size
+        dp = np.abs(decode(gpc, gps) - decode(pc_ref[0, 0], ps_ref[0, 0])).sum()
         ref = o_ref[0, 0].astype(np.float64)
-        got = workloads.bf16_bits_to_f32(o[h, i]).astype(np.float64)
         vmax = vmax_all[h]
-        # natural scores: allow the probability-flip slack of a few blocks
-        tol = (2.0 ** -10 + 1e-4) * vmax + 2.0 ** -7 * np.abs(ref) + 0.01 * vmax
-        assert np.all(np.abs(got - ref) <= tol), (h, i)
-        assert abs(rm[h, i] - rm_ref[0, 0]) <= 1e-5 * max(1.0, abs(rm_ref[0, 0]))
+        bound = out_bound(oracle.FP8_E4M3, lk, vmax_all[h:h + 1], ref[None, None, :], True)[0, 0]
+        bound = bound + 1e-5 * vmax
+        # a probability that moved by dp changes the numerator by at most
+        # dp (|v| + |o|) and the denominator by dp
+        bound = bound + dp * (vmax + np.abs(ref)) / max(float(rs_ref[0, 0]) - dp, 1e-30)
+        got = workloads.bf16_bits_to_f32(to_host(o[h, i])).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= bound), (h, i, float((np.abs(got - ref) / bound).max()))
+        assert abs(float(rm[h, i]) - rm_ref[0, 0]) <= 1e-5 * max(1.0, abs(rm_ref[0, 0]))
+    assert same / total > 0.999, same / total

@@ -1,7 +1,7 @@
 """The five workloads at full size, in the launch configuration the benchmark
-times: GPU results compared with the oracle on sampled rows (blocks run along
-rows, so the oracle on a subset of rows computes exactly those rows' blocks)
-and checked against properties that hold at any size.
+times: every row of every GPU result compared with the oracle (blocks run
+along rows, so the oracle runs on row ranges on all host cores at once), and
+checked against properties that hold at any size.
 """
 import numpy as np
 import pytest
@@ -23,18 +23,14 @@ def mx():
     return m
 
 
-def _sample_rows(nrows, k, seed, extra=()):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(nrows, size=min(k, nrows), replace=False).tolist())
-    rows |= {0, nrows - 1}
-    rows |= set(int(r) for r in extra)
-    return np.array(sorted(rows))
+def _oracle_quantize_all(fmt, x):
+    """oracle.quantize over every row, split across the host's cores."""
+    return oracle.by_rows(lambda a, b: oracle.quantize(fmt, x[a:b]), x.shape[0])
 
 
-def _check_rows(fmt, x_host, rows, gc, gs, ga=None):
-    oc, os_, oa = oracle.quantize(fmt, x_host[rows])
-    assert_bytes_equal(gs[rows], os_, "scales")
-    assert_bytes_equal(gc[rows], oc, "codes", BPB[fmt])
+def _oracle_dequantize_all(fmt, oc, os_, cols, out_dtype):
+    return oracle.by_rows(lambda a, b: oracle.dequantize(fmt, oc[a:b], os_[a:b], None, b - a, cols,
+                                                         out_dtype), oc.shape[0])
 
 
 def test_weights_small_e2m3_all_ops(mx):
@@ -86,12 +82,11 @@ def test_linear_weight_fp6_round_trip(mx, fmt):
     y = mx.dequantize(codes, scales, None, fmt, torch.bfloat16)
     fq = mx.fake_quantize(xd, fmt)
     torch.cuda.synchronize()
-    rows = _sample_rows(x.shape[0], 200, 3)
-    gc, gs = to_host(codes), to_host(scales)
-    _check_rows(f, x, rows, gc, gs)
-    oc, os_, _ = oracle.quantize(f, x[rows])
-    want = oracle.dequantize(f, oc, os_, None, len(rows), x.shape[1], oracle.BF16)
-    assert_bytes_equal(to_host(y)[rows], want, "dequant rows")
+    oc, os_, _ = _oracle_quantize_all(f, x)
+    assert_bytes_equal(to_host(scales), os_, "scales")
+    assert_bytes_equal(to_host(codes), oc, "codes", BPB[f])
+    want = _oracle_dequantize_all(f, oc, os_, x.shape[1], oracle.BF16)
+    assert_bytes_equal(to_host(y), want, "dequantized")
     # at full size: dequantize(quantize(x)) == fake_quantize(x), bitwise
     assert torch.equal(y.view(torch.int16), fq.view(torch.int16))
 
@@ -102,13 +97,12 @@ def test_attention_probabilities_e2m1(mx):
     codes, scales = mx.softmax_quantize(sd, "mxfp4")
     p = mx.dequantize(codes, scales, None, "mxfp4", torch.float32)
     torch.cuda.synchronize()
-    rows = _sample_rows(s.shape[0], 48, 4)
-    oc, os_ = oracle.softmax_quantize(2, s[rows])
-    gc, gs = to_host(codes), to_host(scales)
-    assert_bytes_equal(gs[rows], os_, "scales")
-    assert_bytes_equal(gc[rows], oc, "codes", 16)
-    want_p = oracle.dequantize(2, oc, os_, None, len(rows), s.shape[1], oracle.FP32)
-    assert_bytes_equal(to_host(p)[rows], want_p, "dequantized P")
+    oc, os_ = oracle.by_rows(lambda a, b: oracle.softmax_quantize(2, s[a:b]), s.shape[0])
+    assert_bytes_equal(to_host(scales), os_, "scales")
+    assert_bytes_equal(to_host(codes), oc, "codes", 16)
+    want_p = _oracle_dequantize_all(2, oc, os_, s.shape[1], oracle.FP32)
+    assert_bytes_equal(to_host(p), want_p, "dequantized P")
+    del want_p
     # full size: no sign bit set; the block holding each row's max has byte 125
     sign_bits = (codes & 0x88).any()
     assert not bool(sign_bits)
@@ -129,9 +123,11 @@ def test_activations_dynamic_round_trip(mx, fmt):
     gc, gs = to_host(codes), to_host(scales)
     with np.errstate(invalid="ignore"):
         xf = workloads.bf16_bits_to_f32(x)
-    bad_rows = np.nonzero(~np.isfinite(xf).all(axis=1))[0][:40]
-    rows = _sample_rows(x.shape[0], 150, 5, extra=bad_rows)
-    _check_rows(f, x, rows, gc, gs)
+    oc, os_, _ = _oracle_quantize_all(f, x)
+    assert_bytes_equal(gs, os_, "scales")
+    assert_bytes_equal(gc, oc, "codes", BPB[f])
+    want = _oracle_dequantize_all(f, oc, os_, x.shape[1], oracle.BF16)
+    assert_bytes_equal(to_host(y), want, "dequantized")
     # full size: a block is poisoned exactly when it holds an inf or a NaN
     nonfinite = ~np.isfinite(xf.reshape(x.shape[0], -1, 32)).all(axis=2)
     assert np.array_equal(gs == 0xFF, nonfinite)

@@ -6,14 +6,24 @@ every finite bf16 pattern under every finite scale byte (0..254), or on every
 code under every scale byte for the reverse direction.  The library uses an
 instruction only for the cases asserted here:
 
-  quantize   E2M3 / E3M2 from bf16 (32-wide), E2M1 from bf16 and fp32: bit-
-             exact over the whole finite domain, saturation included.
-             E2M3 / E3M2 from fp32 (two 16-wide operands whose values land
-             at the even and odd code positions): bit-exact on the fp32
-             sample set under a spread of scale bytes.
-             E4M3 from bf16 and fp32: bit-exact for |v| / X < 512 (every
-             value a block can hold) once a rounded magnitude of 0x7F (the
-             instruction does not saturate) is replaced by 0x7E (448).
+  quantize   from bf16 (E2M3 / E3M2 32-wide, E2M1 and E4M3 pairwise): every
+             finite bf16 pattern under every byte 0..254, bit-exact,
+             saturation included.
+             from fp32 (E2M3 / E3M2 as two 16-wide operands whose values
+             land at the even and odd code positions; E2M1 and E4M3
+             pairwise): every rounding class under every byte 0..254.  A
+             round-to-nearest-even conversion of v / X depends only on the
+             exponent, the mantissa bits the target keeps, the first bit
+             below them and whether any lower bit is set; the sweep takes
+             every fp32 exponent field (subnormals included), every pattern
+             of the top 8 mantissa bits (which hold the kept bits and the
+             round bit of every target binade), the low 15 bits as none,
+             the lowest, the highest or all of them set, and both signs:
+             522,240 values x 255 bytes per form, bit-exact for every value
+             a block can hold (|v| / X < 2^(emax + 1)).
+             E4M3 (bf16 and fp32): bit-exact for |v| / X < 512 once a
+             rounded magnitude of 0x7F (the instruction does not saturate)
+             is replaced by 0x7E (448).
   dequantize every code under scale bytes 0..254 is the exact product
              rounded to the output type; byte 255 gives a NaN, which the
              library replaces by the canonical quiet NaN.
@@ -85,6 +95,55 @@ def fp32_set():
     return s[: (s.size // 32) * 32]
 
 
+def fp32_rounding_classes() -> np.ndarray:
+    """Every fp32 exponent field 0..254, every top-8 mantissa pattern, the
+    low 15 bits in {0, 1, 0x4000, 0x7FFF}, both signs (522,240 values)."""
+    e = np.arange(255, dtype=np.uint32)
+    t = np.arange(256, dtype=np.uint32)
+    lo = np.array([0, 1, 0x4000, 0x7FFF], np.uint32)
+    bits = ((e[:, None, None] << 23) | (t[None, :, None] << 15) | lo[None, None, :]).reshape(-1)
+    return np.concatenate([bits, bits | np.uint32(0x80000000)]).view(np.float32)
+
+
+def sweep_fp32(fmt, run, group):
+    """Run `run(values_dev, bytes_dev, nlanes) -> codes [n]` for every byte
+    0..254 over the rounding classes (`group` values per lane) and compare
+    with the bisection nearest-code search; returns (mismatches inside the
+    block domain, mismatches outside it, values checked)."""
+    vals = fp32_rounding_classes()
+    lanes = vals.size // group
+    d_in = dev(vals)
+    v64 = vals.astype(np.float64)
+    absv, sign = np.abs(v64), np.signbit(v64).astype(np.int64) << (brute.CODE_BITS[fmt] - 1)
+    g = brute.finite_grid(fmt)
+    bad_in, bad_out, checked = [], 0, 0
+    chunk = 8  # bytes per launch
+    d_vals = torch.cat([d_in] * chunk)
+    for b0 in range(0, 255, chunk):
+        bs = np.arange(b0, min(b0 + chunk, 255), dtype=np.uint8)
+        sb = dev(np.repeat(bs, lanes))
+        got = run(d_vals[: bs.size * vals.size], sb, bs.size * lanes).reshape(bs.size, -1)
+        for j, b in enumerate(bs):
+            a = absv / 2.0 ** (int(b) - 127)
+            # clamped to the top value: its code; at most half the smallest
+            # nonzero value: code 0 (a tie there goes to the even code 0);
+            # between: the nearest-code search
+            want = np.where(a >= g[-1], g.size - 1, 0) | sign
+            mid = (a > g[1] / 2) & (a < g[-1])
+            want[mid] = brute.encode_sorted(fmt, v64[mid], int(b))
+            inside = a < 2.0 ** (EMAX[fmt] + 1)
+            gj = got[j]
+            if fmt == E4M3:
+                gj = np.where((gj & 0x7F) == 0x7F, gj - 1, gj)  # the library's saturation fix
+            diff = gj != want
+            if diff[inside].any():
+                i = np.nonzero(diff & inside)[0][:3]
+                bad_in.append((int(b), v64[i].tolist(), gj[i].tolist(), want[i].tolist()))
+            bad_out += int((diff & ~inside).sum())
+            checked += vals.size
+    return bad_in, bad_out, checked
+
+
 SCALE_SAMPLE = np.array([0, 1, 2, 5, 60, 100, 117, 120, 124, 125, 126, 127, 128, 129, 130, 135,
                          140, 200, 250, 254], np.uint8)
 
@@ -128,6 +187,36 @@ def test_pk32_fp6_from_bf16_all_patterns_all_scales(lib, kind, fmt):
     want = expected(fmt, vals[m], byte_of[m])
     bad = np.nonzero(got[m] != want)[0]
     assert bad.size == 0, (bad.size, vals[m][bad[:5]], byte_of[m][bad[:5]], got[m][bad[:5]], want[bad[:5]])
+
+
+@pytest.mark.parametrize("kind,fmt", [(0, E2M3), (1, E3M2)], ids=["e2m3", "e3m2"])
+def test_2xpk16_fp6_from_fp32_every_rounding_class_every_scale(lib, kind, fmt):
+    def run(d_vals, sb, nl):
+        out = torch.zeros(nl * 6, dtype=torch.int32, device="cuda")
+        assert lib.probe_q_fp6_f32(kind, d_vals.data_ptr(), sb.data_ptr(), out.data_ptr(), nl) == 0
+        return unpack_stream(out.cpu().numpy().view(np.uint32).reshape(-1, 6), 6, 32).reshape(-1)
+
+    bad_in, bad_out, n = sweep_fp32(fmt, run, 32)
+    assert n == 522240 * 255
+    assert not bad_in, bad_in[:4]
+    print(f"fp6 f32 sweep: {n} values, {bad_out} differ only where |v|/X >= 2^(emax+1)")
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
+def test_pk_fp4_fp8_from_fp32_every_rounding_class_every_scale(lib, fmt):
+    w = 4 if fmt == E2M1 else 8
+    fn = lib.probe_q_fp4_f32 if fmt == E2M1 else lib.probe_q_fp8_f32
+
+    def run(d_vals, sb, nl):
+        out = torch.zeros(nl, dtype=torch.int32, device="cuda")
+        assert fn(d_vals.data_ptr(), sb.data_ptr(), out.data_ptr(), nl) == 0
+        o = out.cpu().numpy().view(np.uint32)
+        return np.stack([o & ((1 << w) - 1), (o >> w) & ((1 << w) - 1)], axis=1).reshape(-1).astype(np.int64)
+
+    bad_in, bad_out, n = sweep_fp32(fmt, run, 2)
+    assert n == 522240 * 255
+    assert not bad_in, bad_in[:4]
+    print(f"pk f32 sweep: {n} values, {bad_out} differ only where |v|/X >= 2^(emax+1)")
 
 
 @pytest.mark.parametrize("kind,fmt", [(0, E2M3), (1, E3M2)], ids=["e2m3", "e3m2"])

@@ -563,3 +563,19 @@ def test_axs6_nonzero_config_decodes_to_nan():
     assert np.all(np.isnan(y[2])) and np.all(np.isnan(y[4]))
     keep = [0, 1, 3, 5, 6, 7]
     assert np.array_equal(y[keep], y0[keep]) and not np.isnan(y0).any()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
+def test_bisection_encoder_equals_exhaustive_search(fmt):
+    """brute.encode_sorted (used for the hardware sweeps) picks the same code
+    as the all-pairs nearest-grid search on random values, every grid point,
+    every midpoint and its fp32 neighbours, signed zeros and saturating
+    values, under several scale bytes."""
+    rng = np.random.default_rng(40 + fmt)
+    g = brute.finite_grid(fmt)
+    mids = (g[:-1] + g[1:]) / 2
+    base = np.concatenate([rng.standard_normal(20000) * g.max() / 2, mids, -mids, g, -g,
+                           np.nextafter(mids, 0), np.nextafter(mids, 1e30), [0.0, -0.0, 1e9, -1e9]])
+    for b in (0, 3, 120, 126, 127, 128, 200, 254):
+        v = (base * 2.0 ** (b - 127)).astype(np.float32).astype(np.float64)
+        assert np.array_equal(brute.encode(fmt, v, b), brute.encode_sorted(fmt, v, b)), b
