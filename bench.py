@@ -132,22 +132,26 @@ def headline(mx, x_np, steps, warmup):
     ms_copy = time_launches(copy, nsets, max(50, steps // 10), 20, min_warm_s=SECONDARY_WARM_S)
     copy_gbs = 2 * in_bytes / ms_copy / 1e6
 
-    # the ceiling of this byte mix: a copy kernel with the quantizer's grid,
-    # loads and stores and no arithmetic (tests/hwprobe/bw_probe.hip), timed
-    # exactly like the quantizer on the same buffers
-    ms_mix = None
-    probe = mix_copy_probe()
+    # the ceiling of this byte mix: copy kernels with the quantizer's bytes
+    # read and written and no arithmetic (tests/hwprobe/bw_probe.hip), in
+    # several access schedules, timed exactly like the quantizer on the same
+    # buffers; and the two halves of the mix alone (reads only, writes only)
+    sched = {}
+    probe = mix_variant_probe()
     if probe is not None:
-        def mix(i):
-            if probe(xs[i].data_ptr(), nb, codes[i].data_ptr(), scales[i].data_ptr(), stream):
-                raise RuntimeError("probe_mix_copy launch failed")
+        sink = torch.empty((nb + 255) // 256, dtype=torch.int32, device="cuda")
+        for v, name in MIX_VARIANTS.items():
+            def mix(i, v=v):
+                if probe(v, xs[i].data_ptr(), nb, codes[i].data_ptr(), scales[i].data_ptr(),
+                         sink.data_ptr(), stream):
+                    raise RuntimeError(f"probe_mix_variant {v} launch failed")
 
-        ms_mix = time_launches(mix, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
-        # the probe wrote its own bytes into the output buffers: set 0 gets
-        # the quantizer's output back for the parity check against the oracle
+            sched[name] = time_launches(mix, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
+        # the probes wrote their own bytes into the output buffers: set 0
+        # gets the quantizer's output back for the parity check
         step(0)
         torch.cuda.synchronize()
-    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, ms_mix
+    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, sched
 
 
 def rows_floor_probe():
@@ -166,18 +170,28 @@ def rows_floor_probe():
     return fn
 
 
-def mix_copy_probe():
-    """probe_mix_copy from the test probe library, or None if it is not built."""
+# access schedules of the byte-mix copy (tests/hwprobe/bw_probe.hip)
+MIX_VARIANTS = {0: "quantizer_grid", 1: "xcd_contiguous", 2: "read_phase_then_write_4_blocks",
+                3: "read_phase_then_write_4_blocks_xcd", 7: "nontemporal_stores",
+                11: "coalesced_1KB_instructions", 4: "reads_only", 5: "writes_only",
+                10: "reads_only_coalesced", 9: "writes_only_coalesced"}
+MIX_COPIES = ("quantizer_grid", "xcd_contiguous", "read_phase_then_write_4_blocks",
+              "read_phase_then_write_4_blocks_xcd", "nontemporal_stores",
+              "coalesced_1KB_instructions")
+
+
+def mix_variant_probe():
+    """probe_mix_variant from the test probe library, or None if it is not built."""
     import ctypes
     path = os.path.join(ROOT, "tests", "hwprobe", "libcvtprobe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    if not hasattr(lib, "probe_mix_copy"):
+    if not hasattr(lib, "probe_mix_variant"):
         return None
-    fn = lib.probe_mix_copy
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                   ctypes.c_void_p]
+    fn = lib.probe_mix_variant
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_void_p]
     fn.restype = ctypes.c_int
     return fn
 
@@ -643,8 +657,8 @@ def main():
         return
 
     x = workloads.linear_weight()
-    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs, ms_mix = headline(mx, x, args.steps,
-                                                                         args.warmup)
+    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs, sched = headline(mx, x, args.steps,
+                                                                        args.warmup)
     achieved = alg_b / ms / 1e6
     digest = source_digest()
     out = {
@@ -674,13 +688,24 @@ def main():
                                        "write bytes / time), same buffers and rotation; a "
                                        "reference rate, not a ceiling"},
     }
-    if ms_mix is not None:
-        out["mix_ceiling"] = {
-            "us": round(ms_mix * 1e3, 3), "GBps": round(alg_b / ms_mix / 1e6, 1),
-            "frac_of_peak": round(alg_b / ms_mix / 1e6 / HBM_PEAK_GBS, 4),
-            "headline_frac_of_ceiling": round(ms_mix / ms, 4),
-            "note": "copy kernel with the quantizer's grid, loads and stores and no arithmetic "
-                    "(tests/hwprobe/bw_probe.hip), same buffers, rotation, warm-up and steps"}
+    if sched:
+        best = min(MIX_COPIES, key=lambda k: sched[k])
+        serial = min(sched["reads_only"], sched["reads_only_coalesced"]) + \
+            min(sched["writes_only"], sched["writes_only_coalesced"])
+        out["best_mix_ceiling"] = {
+            "us": round(sched[best] * 1e3, 3), "schedule": best,
+            "frac_of_peak": round(alg_b / sched[best] / 1e6 / HBM_PEAK_GBS, 4),
+            "headline_frac_of_ceiling": round(sched[best] / ms, 4),
+            "schedules_us": {k: round(v * 1e3, 3) for k, v in sched.items()},
+            "serial_bound_us": round(serial * 1e3, 3),
+            "serial_bound_frac_of_peak": round(alg_b / serial / 1e6 / HBM_PEAK_GBS, 4),
+            "read_only_GBps": round(in_b / min(sched["reads_only"],
+                                               sched["reads_only_coalesced"]) / 1e6, 1),
+            "write_only_GBps": round((alg_b - in_b) / min(sched["writes_only"],
+                                                          sched["writes_only_coalesced"]) / 1e6, 1),
+            "note": "copy kernels moving the quantizer's bytes with no arithmetic, in each access "
+                    "schedule (tests/hwprobe/bw_probe.hip), same buffers, rotation, warm-up and "
+                    "steps; serial bound = the fastest reads alone plus the fastest writes alone"}
     import oracle
     threads = oracle.worker_threads()
     failed = []

@@ -83,3 +83,221 @@ extern "C" int probe_rows_floor(const void* s, int64_t rows, int64_t cols, void*
                      static_cast<uint2*>(codes), scales);
   return (int)hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Other access schedules for the same byte mix (64 bytes read, 24 + 1
+// written per 32-value block), to find the fastest one this HBM allows:
+//   variant 0  the quantizer's schedule (mix_copy above)
+//   variant 1  the same, with workgroups renumbered so that each of the 8
+//              XCDs (which receive consecutive workgroups in turn) covers
+//              one contiguous eighth of the tensor
+//   variant 2  4 blocks per lane, all 16 loads of a lane issued before any
+//              store; the workgroup's 1024 blocks then leave as one
+//              contiguous 24 KB run of codes (staged in LDS) and 1 KB of
+//              scales
+//   variant 3  variant 2 with the XCD renumbering
+//   variant 4  read only (the same loads as variant 0, one dword written
+//              per workgroup), the read half of the mix
+//   variant 5  write only (the same stores as variant 0, nothing read),
+//              the write half of the mix
+//   variants 6, 7, 8  variant 0 with device-scope (sc1), nontemporal (nt)
+//              and system-scope (sc0 sc1) stores
+//   variants 9, 10, 11  writes only, reads only, and the whole mix, with
+//              every instruction of a wave covering 1 KB of consecutive
+//              bytes (whole workgroups of 256 blocks only)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t xcd_order(int64_t wg, int64_t total) {
+  return (total & 7) == 0 ? (wg & 7) * (total >> 3) + (wg >> 3) : wg;
+}
+
+// Store cache policies: 0 the default; 1 device scope (relaxed atomic
+// stores at agent scope, which carry the sc1 bit: written through the
+// XCD's L2); 2 nontemporal (the nt bit); 3 system scope (sc0 sc1).
+template <int POL>
+__device__ __forceinline__ void store_u64(uint64_t* p, uint64_t v) {
+  if constexpr (POL == 0) *p = v;
+  else if constexpr (POL == 1) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else if constexpr (POL == 2) __builtin_nontemporal_store(v, p);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+template <int POL>
+__device__ __forceinline__ void store_u8(uint8_t* p, uint8_t v) {
+  if constexpr (POL == 0) *p = v;
+  else if constexpr (POL == 1) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else if constexpr (POL == 2) __builtin_nontemporal_store(v, p);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <bool XCD, int POL = 0>
+__global__ __launch_bounds__(256) void mix_copy_grid(const uint4* __restrict__ x, int64_t nb,
+                                                     uint64_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
+  const int64_t wg = XCD ? xcd_order(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  const int64_t b = wg * 256 + threadIdx.x;
+  if (b >= nb) return;
+  const uint4 q0 = x[4 * b], q1 = x[4 * b + 1], q2 = x[4 * b + 2], q3 = x[4 * b + 3];
+  const uint32_t o0 = q0.x ^ q2.z, o1 = q0.y ^ q2.w, o2 = q0.z ^ q3.x, o3 = q0.w ^ q3.y;
+  const uint32_t o4 = q1.x ^ q1.z ^ q3.z, o5 = q1.y ^ q1.w ^ q3.w ^ q2.x ^ q2.y;
+  store_u64<POL>(codes + 3 * b, o0 | ((uint64_t)o1 << 32));
+  store_u64<POL>(codes + 3 * b + 1, o2 | ((uint64_t)o3 << 32));
+  store_u64<POL>(codes + 3 * b + 2, o4 | ((uint64_t)o5 << 32));
+  store_u8<POL>(scales + b, (uint8_t)(o0 ^ o5));
+}
+
+template <bool XCD>
+__global__ __launch_bounds__(256) void mix_copy_phase(const uint4* __restrict__ x, int64_t nb,
+                                                      uint4* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  constexpr int C = 4;  // blocks per lane
+  __shared__ uint32_t lds[256 * C * 6];
+  const int t = threadIdx.x;
+  const int64_t wg = XCD ? xcd_order(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  const int64_t b0 = wg * 256 * C;
+  uint4 q[C][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int64_t b = b0 + 256 * c + t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[c][i] = b < nb ? x[4 * b + i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int lb = 256 * c + t;  // block within the workgroup's chunk
+    uint32_t* o = lds + 6 * lb;
+    o[0] = q[c][0].x ^ q[c][2].z; o[1] = q[c][0].y ^ q[c][2].w; o[2] = q[c][0].z ^ q[c][3].x;
+    o[3] = q[c][0].w ^ q[c][3].y; o[4] = q[c][1].x ^ q[c][1].z ^ q[c][3].z;
+    o[5] = q[c][1].y ^ q[c][1].w ^ q[c][3].w ^ q[c][2].x ^ q[c][2].y;
+    const int64_t b = b0 + lb;
+    if (b < nb) scales[b] = (uint8_t)(o[0] ^ o[5]);
+  }
+  __syncthreads();
+  // the chunk's codes: 256 * C * 24 bytes = 384 * C 16-byte pieces
+  const int64_t valid = (nb - b0 < 256 * C ? nb - b0 : 256 * C) * 24 / 16;  // whole pieces
+  const uint4* l4 = reinterpret_cast<const uint4*>(lds);
+#pragma unroll
+  for (int i = 0; i < (384 * C) / 256; ++i) {
+    const int p = 256 * i + t;
+    if (p < valid) codes[b0 * 24 / 16 + p] = l4[p];
+  }
+}
+
+__global__ __launch_bounds__(256) void mix_read_only(const uint4* __restrict__ x, int64_t nb,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  if (b < nb) {
+    const uint4 q0 = x[4 * b], q1 = x[4 * b + 1], q2 = x[4 * b + 2], q3 = x[4 * b + 3];
+    acc = q0.x ^ q0.y ^ q0.z ^ q0.w ^ q1.x ^ q1.y ^ q1.z ^ q1.w ^ q2.x ^ q2.y ^ q2.z ^ q2.w ^
+          q3.x ^ q3.y ^ q3.z ^ q3.w;
+  }
+  // a store that depends on every loaded word keeps every load alive; it
+  // happens only for one value, so almost nothing is written
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void mix_write_only(int64_t nb, uint2* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  const uint32_t v = (uint32_t)b * 2654435761u;
+  codes[3 * b] = make_uint2(v, v + 1);
+  codes[3 * b + 1] = make_uint2(v + 2, v + 3);
+  codes[3 * b + 2] = make_uint2(v + 4, v + 5);
+  scales[b] = (uint8_t)v;
+}
+
+// Fully coalesced forms: every load or store instruction of a wave covers
+// 64 consecutive 16-byte pieces (1 KB).  A workgroup's 256 blocks are 1024
+// input pieces, 384 code pieces and 16 scale pieces.
+template <bool READ, bool WRITE>
+__global__ __launch_bounds__(256) void mix_coalesced(const uint4* __restrict__ x, int64_t nb,
+                                                     uint4* __restrict__ codes,
+                                                     uint4* __restrict__ scales,
+                                                     uint32_t* __restrict__ sink) {
+  const int t = threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * 256;
+  if (b0 + 256 > nb) return;  // whole workgroups only (timing probe)
+  uint4 q[4] = {};
+  if constexpr (READ) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = x[4 * b0 + 256 * i + t];
+  }
+  uint4 o0 = make_uint4(q[0].x ^ q[2].z, q[0].y ^ q[2].w, q[0].z ^ q[3].x, q[0].w ^ q[3].y);
+  uint4 o1 = make_uint4(q[1].x ^ q[1].z, q[1].y ^ q[1].w, q[3].z ^ q[2].x, q[3].w ^ q[2].y);
+  if constexpr (!READ) {
+    o0 = make_uint4(t, t + 1, t + 2, t + 3);
+    o1 = make_uint4(t + 4, t + 5, t + 6, t + 7);
+  }
+  if constexpr (WRITE) {
+    uint4* c = codes + b0 * 24 / 16;
+    c[t] = o0;
+    if (t < 128) c[256 + t] = o1;
+    if (t < 16) scales[b0 / 16 + t] = make_uint4(o0.x ^ o1.y, o0.y, o0.z, o0.w ^ o1.x);
+  } else {
+    const uint32_t acc = o0.x ^ o0.y ^ o0.z ^ o0.w ^ o1.x ^ o1.y ^ o1.z ^ o1.w;
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+  }
+}
+
+// variant as above; x: nb * 64 bytes, codes: nb * 24 bytes (16-byte
+// aligned), scales: nb bytes, sink: at least ceil(nb / 256) dwords (variant 4
+// only).  Returns hipGetLastError(), or -1 for an unknown variant.
+extern "C" int probe_mix_variant(int variant, const void* x, int64_t nb, void* codes,
+                                 uint8_t* scales, uint32_t* sink, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nb < 1) return -1;
+  const int64_t g1 = (nb + 255) / 256;          // one block per lane
+  const int64_t g4 = (nb + 1023) / 1024;        // four blocks per lane
+  const int64_t g1x = (g1 + 7) / 8 * 8;         // padded to whole XCD rounds
+  const int64_t g4x = (g4 + 7) / 8 * 8;
+  if (g1x > 0x7FFFFFFF) return -1;
+  const uint4* xi = static_cast<const uint4*>(x);
+  switch (variant) {
+    case 0: return probe_mix_copy(x, nb, codes, scales, stream);
+    case 1:
+      hipLaunchKernelGGL((mix_copy_grid<true, 0>), dim3((unsigned)g1x), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales);
+      break;
+    case 6:
+      hipLaunchKernelGGL((mix_copy_grid<false, 1>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales);
+      break;
+    case 7:
+      hipLaunchKernelGGL((mix_copy_grid<false, 2>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales);
+      break;
+    case 8:
+      hipLaunchKernelGGL((mix_copy_grid<false, 3>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales);
+      break;
+    case 2:
+      hipLaunchKernelGGL(mix_copy_phase<false>, dim3((unsigned)g4), dim3(256), 0, st, xi, nb,
+                         static_cast<uint4*>(codes), scales);
+      break;
+    case 3:
+      hipLaunchKernelGGL(mix_copy_phase<true>, dim3((unsigned)g4x), dim3(256), 0, st, xi, nb,
+                         static_cast<uint4*>(codes), scales);
+      break;
+    case 4:
+      hipLaunchKernelGGL(mix_read_only, dim3((unsigned)g1), dim3(256), 0, st, xi, nb, sink);
+      break;
+    case 5:
+      hipLaunchKernelGGL(mix_write_only, dim3((unsigned)g1), dim3(256), 0, st, nb,
+                         static_cast<uint2*>(codes), scales);
+      break;
+    case 9:
+      hipLaunchKernelGGL((mix_coalesced<false, true>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint4*>(codes), reinterpret_cast<uint4*>(scales), sink);
+      break;
+    case 10:
+      hipLaunchKernelGGL((mix_coalesced<true, false>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint4*>(codes), reinterpret_cast<uint4*>(scales), sink);
+      break;
+    case 11:
+      hipLaunchKernelGGL((mix_coalesced<true, true>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint4*>(codes), reinterpret_cast<uint4*>(scales), sink);
+      break;
+    default: return -1;
+  }
+  return (int)hipGetLastError();
+}
