@@ -10,9 +10,10 @@
 //
 // Work split: one workgroup of 4 waves per (head, 128 queries); each wave
 // owns 32 queries and walks the keys in tiles of 64:
-//   S^T  = K_tile * Q^T      8+8 bf16 32x32x16 MFMAs (two 32-key halves)
-//   swap                     v_permlane32_swap gives each lane the 32 scores
-//                            of one (query, 32-key block) pair
+//   S^T  = K_tile * Q^T      8+8 bf16 32x32x16 MFMAs whose A rows are the
+//                            tile's keys in a permuted order, chosen so that
+//                            each lane receives the 32 scores of one
+//                            (query, 32-key block) pair with no exchange
 //   t    = S * scale; tile max; rescale O and l when the maximum grows
 //   p    = exp_ref(t - m); block scale byte; 16 E2M1 codes per lane, which
 //          are exactly the lane's B operand of the block-scaled MFMA
@@ -61,11 +62,26 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // queries per workgroup
 constexpr int kKBytes = kTile * 2 * kD;  // one K tile in LDS: 64 rows of 256 B
 
+// Score layout.  The two 32x32 score MFMAs of a tile give lane (col, h) the
+// output rows rho = 8g + 4h + e (g = 0..3, e = 0..3) of column col.  The
+// first MFMA's A row rho holds key 32h + 8g + e of the tile and the
+// second's key 32h + 8g + 4 + e, so lane half h ends up with exactly the
+// keys of the tile's block h: accumulator r of the first MFMA is key
+// 8(r/4) + r%4 of the block and of the second key 8(r/4) + 4 + r%4.  A lane
+// therefore reads K row kperm(col) = 32((col/4) % 2) + 8(col/8) + col%4 for
+// the first MFMA and kperm(col) + 4 for the second.
+__device__ __forceinline__ int kperm(int col) {
+  return 32 * ((col >> 2) & 1) + 8 * (col >> 3) + (col & 3);
+}
+
 // LDS layouts.  Tiles arrive by direct global->LDS loads, where lane i of
 // a wave writes the 16-byte slot i of a contiguous run (a 12-byte load
 // fills the first 12 bytes of its slot), so conflict-free reads come from
 // XOR-swizzling the slot order inside a row instead of padding.
-//   K: row r (key), 16-B chunk L (8 values of one row) in slot L ^ (r % 16).
+//   K: row r (key), 16-B chunk L (8 values of one row) in slot L ^ kswz(r),
+//      kswz(r) = r%4 + 4((r/32) % 2) + 8((r/8) % 2): the 16 lanes of one
+//      LDS read cycle (columns 16c..16c+15) read rows kperm(col) (+ 4),
+//      whose kswz is col % 16, so they hit 16 distinct slots.
 //   V^T, two blocks of row d: E4M3 4 chunks of 16 B, E2M3/E3M2 4 chunks of
 //      12 B (half a block each), chunk L in slot L ^ ((d / 2) % 4); E2M1 2
 //      chunks of 16 B, chunk L in slot L ^ ((d / 4) % 2).
@@ -74,6 +90,9 @@ template <> struct VTile<0> {
   static constexpr int BPB = 32, CH = 16, CPR = 4;
   __device__ static int swz(int d) { return (d >> 1) & 3; }
 };
+__device__ __forceinline__ int kswz(int r) {
+  return (r & 3) | (((r >> 5) & 1) << 2) | (((r >> 3) & 1) << 3);
+}
 template <> struct VTile<2> {
   static constexpr int BPB = 24, CH = 12, CPR = 4;
   __device__ static int swz(int d) { return (d >> 1) & 3; }
@@ -84,25 +103,44 @@ template <> struct VTile<4> {
   __device__ static int swz(int d) { return (d >> 2) & 1; }
 };
 
-// The A operand (V^T row d, lane half h) of the block-scaled MFMA from the
-// LDS copy of the tile's two blocks of that row.
+// The A operand (V^T row d = 32T + col, lane half h) of the block-scaled
+// MFMA from the LDS copy of the tile's two blocks of that row.  The swizzle
+// of row d depends only on col, so a lane's two chunk offsets inside row
+// col (v_offsets) serve every T; rows 32T + col are 32T rows further on,
+// which the LDS reads take as immediate offsets.
 template <int VF>
-__device__ __forceinline__ i32x8_t load_v_operand(const uint8_t* vt, int d, int h) {
+__device__ __forceinline__ void v_offsets(int col, int h, uint32_t& lo, uint32_t& hi) {
   using L = VTile<VF>;
-  const uint8_t* row = vt + d * L::CPR * 16;
-  const int z = L::swz(d);
+  const int z = L::swz(col);
+  const int base = col * L::CPR * 16;
+  if constexpr (VF == 0) {
+    lo = (uint32_t)(base + 16 * (h ^ z));
+    hi = (uint32_t)(base + 16 * ((2 + h) ^ z));
+  } else if constexpr (VF == 4) {
+    lo = hi = (uint32_t)(base + 16 * (h ^ z));
+  } else {
+    lo = (uint32_t)(base + 16 * ((2 * h) ^ z));
+    hi = (uint32_t)(base + 16 * ((2 * h + 1) ^ z));
+  }
+}
+
+template <int VF>
+__device__ __forceinline__ i32x8_t load_v_operand(const uint8_t* vt, int T, uint32_t lo_off,
+                                                  uint32_t hi_off) {
+  using L = VTile<VF>;
+  const uint8_t* rows = vt + T * 32 * L::CPR * 16;
   i32x8_t a = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (VF == 0) {
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(row + 16 * (h ^ z));
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(row + 16 * ((2 + h) ^ z));
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(rows + lo_off);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(rows + hi_off);
     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
     a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
   } else if constexpr (VF == 4) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + 16 * (h ^ z));
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(rows + lo_off);
     a[0] = w[0]; a[1] = w[1]; a[2] = w[2]; a[3] = w[3];
   } else {
-    const u32x3_t lo = *reinterpret_cast<const u32x3_t*>(row + 16 * ((2 * h) ^ z));
-    const u32x3_t hi = *reinterpret_cast<const u32x3_t*>(row + 16 * ((2 * h + 1) ^ z));
+    const u32x3_t lo = *reinterpret_cast<const u32x3_t*>(rows + lo_off);
+    const u32x3_t hi = *reinterpret_cast<const u32x3_t*>(rows + hi_off);
     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = hi[0]; a[4] = hi[1]; a[5] = hi[2];
   }
   return a;
@@ -129,7 +167,7 @@ struct TileLoader {
   const uint8_t* kh;  // this head's K
   const uint8_t* vh;  // this head's V^T codes
   int64_t vstep;      // bytes of the V^T rows one round of instructions covers
-  uint32_t koff;      // lane's K byte offset inside a tile (instruction 0)
+  uint32_t koff[2];   // lane's K byte offset inside a tile (instruction 0; rows 0..31, 32..63)
   uint32_t voff;      // lane's V byte offset (instruction 0, tile 0)
   uint32_t vhalf;     // bytes back to the first block when the lane's chunk is in the second
   int lk, nbk, wave;
@@ -142,11 +180,13 @@ struct TileLoader {
     kh = reinterpret_cast<const uint8_t*>(k) + (int64_t)bh * lk * (2 * kD);
     vh = vc + (int64_t)bh * kD * nbk * L::BPB;
     vstep = (int64_t)(kThreads / L::CPR) * nbk * L::BPB;
-    // K chunk c = 64 (kWaves n + wave) + lane: row 4 kWaves n + 4 wave +
-    // lane / 16, slot lane % 16, logical chunk slot ^ (row % 16) (n does
-    // not change it: 4 kWaves is a multiple of 16)
+    // K chunk c = 64 (4 n + wave) + lane: row 16 n + 4 wave + lane / 16,
+    // slot lane % 16, logical chunk slot ^ kswz(row); kswz changes with n
+    // only through row bit 5 (n >= 2)
+    static_assert(kWaves == 4, "the K swizzle offsets assume 16 rows per round");
     const int r0 = 4 * wave + (lane >> 4);
-    koff = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ (r0 & 15)));
+    koff[0] = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ kswz(r0)));
+    koff[1] = (uint32_t)(r0 * 256 + 16 * ((lane & 15) ^ kswz(r0 + 32)));
     // V chunk c = 64 (kWaves n + wave) + lane: row c / CPR, slot c % CPR (n
     // adds kThreads / CPR rows and does not change the swizzle)
     const int c0 = wave * 64 + lane;
@@ -166,7 +206,7 @@ struct TileLoader {
       // rows 32.. of a 32-key last tile do not exist: re-read rows 0..
       const int r = n * kRowsPerRound;
       const uint8_t* base = kt + (int64_t)(r - ((!two && r >= 32) ? 32 : 0)) * (2 * kD);
-      lds_load16(base + koff, ksb + (kWaves * n + wave) * 64 * 16);
+      lds_load16(base + koff[n >= 2], ksb + (kWaves * n + wave) * 64 * 16);
     }
     const uint32_t vo = two ? voff : voff - vhalf;
     const uint8_t* vt = vh + (int64_t)kb0 * L::BPB;
@@ -203,6 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
   // wave) stay in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, h = lane >> 5;
+  const int krow = kperm(col);  // this lane's A row of the score MFMAs
 
   // Workgroup order: the hardware deals consecutive workgroups round-robin
   // to the 8 XCDs, so renumber them to give each XCD a contiguous range of
@@ -237,6 +278,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
   }
   float m = -INFINITY;
   const i32x8_t ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
+  // the B operand of the PV products: E2M1 codes in dwords 0..3, the rest
+  // unused by FP4 and kept zero across tiles
+  i32x8_t pb = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint32_t vlo, vhi;
+  v_offsets<VF>(col, h, vlo, vhi);
 
   // V^T scale bytes of tile jt for row d = tid (tid < 128): the second
   // address repeats the first when the tile has one block, so both loads
@@ -272,30 +318,31 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       }
     }
 
-    // S^T for keys key0 .. +31 (s0) and key0+32 .. +63 (s1)
+    // S^T of the tile: with the A rows in kperm order, s0[r] of lane half h
+    // is key 32h + 8(r/4) + r%4 of the tile and s1[r] key 32h + 8(r/4) + 4 +
+    // r%4
     f32x16_t s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // logical chunk 8h + i of rows col and 32 + col (same r % 16)
+      // logical chunk 8h + i of rows kperm(col) and kperm(col) + 4, whose
+      // kswz are both col % 16
       const int pch = ((8 * h + i) ^ (col & 15)) * 16;
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kt + col * 256 + pch);
-      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kt + (32 + col) * 256 + pch);
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(kt + krow * 256 + pch);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(kt + (krow + 4) * 256 + pch);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), qf[i], s0, 0,
                                                    0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qf[i], s1, 0,
                                                    0, 0);
     }
-    // After the swap every lane holds block h of the tile for its query:
-    // x[r] is key 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4.
+    // every lane holds block h of the tile for its query: x[r] is key
+    // 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4
     float x[16], y[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0[r]),
-                                                       __float_as_uint(s1[r]), false, false);
-      x[r] = __uint_as_float(sw[0]) * scale;
-      y[r] = __uint_as_float(sw[1]) * scale;
+      x[r] = s0[r] * scale;
+      y[r] = s1[r] * scale;
     }
     const bool dead = !two && h;  // the block past lk of a 32-key last tile
 
@@ -313,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const bool careful = __any(mt != mt || !(__builtin_fabsf(fmaxf(m, mt)) < INFINITY));
-    if (careful) {
+    if (__builtin_expect(careful, 0)) {
       // the maximum the method defines skips NaN scores
       mt = x[0];
 #pragma unroll
@@ -363,7 +410,23 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
 #pragma unroll
       for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
       byte = scale_byte_from_amax<F_E2M1>(amax);
-      encode_f32<F_E2M1>(v, scale_operand(byte), pk);
+      // the four converts of a dword write its four bytes, so the dword's
+      // previous contents do not matter: they start from pb's own dwords
+      // (no register has to be cleared first)
+      const float sc = scale_operand(byte);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w = (uint32_t)pb[q];
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(v[8 * q]),
+                                                     __uint_as_float(v[8 * q + 1]), sc, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(v[8 * q + 2]),
+                                                     __uint_as_float(v[8 * q + 3]), sc, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(v[8 * q + 4]),
+                                                     __uint_as_float(v[8 * q + 5]), sc, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(v[8 * q + 6]),
+                                                     __uint_as_float(v[8 * q + 7]), sc, 3);
+        pk[q] = w;
+      }
     } else {
       // EFQ reading, no exp: u = (t - m) log2 e; the MX scale rule on 2^max u;
       // code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5)).  A NaN u
@@ -398,16 +461,20 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       }
       byte = U != U ? 0xFFu : (uint32_t)b;
     }
-    const bool zero = dead || byte == 0xFFu;  // no codes (a NaN block keeps 0xFF)
-    byte = dead ? 0u : byte;
+    // blocks without codes: past lk (byte 0) and NaN blocks (0xFF), which
+    // only a 32-key last tile or the careful path can produce (uniform)
+    if (__builtin_expect(!two || careful, 0)) {
+      const bool zero = dead || byte == 0xFFu;
+      byte = dead ? 0u : byte;
 #pragma unroll
-    for (int e = 0; e < Fmt<F_E2M1>::W; ++e) pk[e] = zero ? 0u : pk[e];
-    const i32x8_t pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+      for (int e = 0; e < Fmt<F_E2M1>::W; ++e) pk[e] = zero ? 0u : pk[e];
+    }
+    pb[0] = (int)pk[0]; pb[1] = (int)pk[1]; pb[2] = (int)pk[2]; pb[3] = (int)pk[3];
 
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const int dd = 32 * T + col;
-      const i32x8_t va = load_v_operand<VF>(vt, dd, h);
+      const i32x8_t va = load_v_operand<VF>(vt, T, vlo, vhi);
       acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc[T], VF, 4, 0,
                                                                (int)st[2 * dd + h], 0, (int)byte);
     }
