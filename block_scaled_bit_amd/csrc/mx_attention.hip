@@ -396,12 +396,14 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
             v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos<true>(y[4 * g + e] - m));
           }
       } else {
+        // no NaN score and a finite maximum: the exp without its clamp,
+        // checked below
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
-            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+            v[8 * g + e] = __float_as_uint(exp_ref_nonpos_unclamped(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos_unclamped(y[4 * g + e] - m));
           }
       }
       // p >= 0 or NaN, so the bit patterns order as the values and a NaN
@@ -409,6 +411,20 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       uint32_t amax = 0u;
 #pragma unroll
       for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
+      if (__builtin_expect(!careful && __any(amax >= 0x7F800000u), 0)) {
+        // a score far below the maximum (or -inf) left the unclamped range:
+        // the clamped exp, for the whole wave
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+          }
+        amax = 0u;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
+      }
       byte = scale_byte_from_amax<F_E2M1>(amax);
       // the four converts of a dword write its four bytes, so the dword's
       // previous contents do not matter: they start from pb's own dwords

@@ -43,4 +43,33 @@ __device__ __forceinline__ float exp_ref_nonpos(float d) {
   return __builtin_ldexpf(p, (int)nf);
 }
 
+// The same sequence without the clamp, for callers that check the results.
+// For d >= -104 it is exp_ref_nonpos(d).  For -2^20 <= d < -104 it is 0 or
+// 2^-149 where exp_ref_nonpos gives 0: n <= -150, the reduced argument stays
+// within [-0.5, 0.5], so p * 2^n is at most 0.83 * 2^-149.  For d < -2^20 or
+// d = -inf it is +0, -0, +-inf or NaN (a huge n or a garbage reduction).  So
+// every result is either one that encodes like exp_ref_nonpos's (0 and
+// 2^-149 both round to the zero code under any block scale, and both give a
+// block of nothing else the scale byte 0), or has a bit pattern of at least
+// 0x7F800000, which the caller detects and then recomputes with the clamp.
+__device__ __forceinline__ float exp_ref_nonpos_unclamped(float d) {
+  const float kLog2e = 0x1.715476p+0f;
+  const float kLn2Hi = 0x1.62e400p-1f;
+  const float kLn2Lo = 0x1.7f7d1cp-20f;
+  const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
+              k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
+  const float nf = __builtin_rintf(d * kLog2e);
+  float r = __builtin_fmaf(-nf, kLn2Hi, d);
+  r = __builtin_fmaf(-nf, kLn2Lo, r);
+  float p = k7;
+  p = __builtin_fmaf(p, r, k6);
+  p = __builtin_fmaf(p, r, k5);
+  p = __builtin_fmaf(p, r, k4);
+  p = __builtin_fmaf(p, r, k3);
+  p = __builtin_fmaf(p, r, k2);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)nf);
+}
+
 }  // namespace mxk
