@@ -299,3 +299,37 @@ def test_full_size_natural_scores_rows(mx):
         assert np.all(np.abs(got - ref) <= bound), (h, i, float((np.abs(got - ref) / bound).max()))
         assert abs(float(rm[h, i]) - rm_ref[0, 0]) <= 1e-5 * max(1.0, abs(rm_ref[0, 0]))
     assert same / total > 0.999, same / total
+
+
+@pytest.mark.parametrize("rule", ["exp", "efq"])
+def test_scores_far_below_the_maximum(mx, rule):
+    """Scores 100 to 10^6 below the running maximum and -inf scores (fp32
+    overflow of q . k) with a finite maximum: the fast path's unclamped exp
+    leaves its range there and must fall back to the clamped one; the
+    probability blocks equal the oracle's bit for bit."""
+    efq = rule == "efq"
+    rng = np.random.default_rng(17)
+    heads, lq, lk = 1, 64, 192
+    qf = rng.integers(-12, 13, (heads, lq, D)).astype(np.float32) / 4
+    kf = rng.integers(-12, 13, (heads, lk, D)).astype(np.float32) / 4
+    # dims 0 and 1 are zero in every query and key but the ones named: query 5's
+    # score with key 70 overflows to -inf; query 9's scores with keys 33
+    # and 150 are -2^60 and -2^10 (the other scores are a few units)
+    qf[:, :, :2] = 0.0
+    kf[:, :, :2] = 0.0
+    qf[0, 5, 0] = 2.0 ** 100
+    kf[0, 70, 0] = -(2.0 ** 100)
+    qf[0, 9, 1] = 2.0 ** 30
+    kf[0, 33, 1] = -(2.0 ** 30)
+    kf[0, 150, 1] = -(2.0 ** -20)
+    q, k = bf16(qf), bf16(kf)
+    vc, vs = v_input(rng, heads, lk, oracle.FP6_E2M3)
+    for scale in (np.float32(0.125), np.float32(40.0), np.float32(3000.0)):
+        _, rm_ref, _, pc_ref, ps_ref = oracle.attention_fwd(oracle.FP6_E2M3, q, k, vc, vs, scale,
+                                                            64, oracle.FP32, efq=efq)
+        o, rm, rs, pc, ps = run_gpu(mx, oracle.FP6_E2M3, q, k, vc, vs, scale, torch.float32,
+                                    efq=efq)
+        assert np.array_equal(ps, ps_ref), scale
+        assert np.array_equal(pc, pc_ref), scale
+        assert np.array_equal(rm, rm_ref), scale
+        assert np.all(np.isfinite(o)), scale
