@@ -196,6 +196,22 @@ def mix_variant_probe():
     return fn
 
 
+def bytes_copy_probe():
+    """probe_bytes_copy from the test probe library, or None if it is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "tests", "hwprobe", "libcvtprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    if not hasattr(lib, "probe_bytes_copy"):
+        return None
+    fn = lib.probe_bytes_copy
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def host(t):
     """Device tensor -> numpy (bf16 as uint16 bit patterns)."""
     import numpy as np
@@ -220,6 +236,7 @@ class Secondary:
         self.threads = threads
         self.res = {}
         self.failed = []
+        self.copy = bytes_copy_probe()
 
     def launch(self, name, fn):
         """fn(i) -> mx status; a nonzero status raises instead of being timed."""
@@ -231,12 +248,41 @@ class Secondary:
                 raise mx.MxError(st, name)
         return call
 
-    def time(self, name, fn, nsets, in_b, out_b, note, steps=None, warm=3):
+    def time(self, name, fn, nsets, in_b, out_b, note, steps=None, warm=3, copy_bpb=None):
+        """copy_bpb = (bytes read, bytes written) per 32-value block: also
+        time a plain copy of those byte counts (tests/hwprobe/bw_probe.hip,
+        every instruction covering 1 KB of consecutive bytes) on buffers of
+        its own, as the row's streaming floor."""
         ms = time_launches(self.launch(name, fn), nsets, steps or self.k, warm,
                            min_warm_s=SECONDARY_WARM_S)
         self.res[name] = {"us": round(ms * 1e3, 2), "input_GBps": round(in_b / ms / 1e6, 1),
                           "hbm_frac": round((in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS, 4),
                           "bytes": in_b + out_b, "workload": note}
+        if copy_bpb is not None and self.copy is not None:
+            ib, ob = copy_bpb
+            nb = (in_b + out_b) // (ib + ob)
+            ms_c = self.copy_floor(nb, ib, ob, steps or self.k, warm)
+            self.res[name].update(copy_us=round(ms_c * 1e3, 2), frac_of_copy=round(ms_c / ms, 4),
+                                  copy_note=f"{ib} B read and {ob} B written per block, copied "
+                                            "with 1 KB instructions")
+        return ms
+
+    def copy_floor(self, nb, ib, ob, steps, warm):
+        torch = self.torch
+        per = -(-nb * ib // 16) * 16 + -(-nb * ob // 16) * 16
+        n = rotation_sets(per)
+        xs = [torch.empty(-(-nb * ib // 16) * 16, dtype=torch.uint8, device="cuda")
+              for _ in range(n)]
+        ys = [torch.empty(-(-nb * ob // 16) * 16, dtype=torch.uint8, device="cuda")
+              for _ in range(n)]
+        st = self.stream
+
+        def f(i):
+            return self.copy(xs[i].data_ptr(), nb, ib, ys[i].data_ptr(), ob, st)
+
+        ms = time_launches(self.launch("probe_bytes_copy", f), n, steps, warm,
+                           min_warm_s=SECONDARY_WARM_S)
+        del xs, ys
         return ms
 
     def oracle(self, fn, rows):
@@ -288,9 +334,11 @@ def secondary(mx, steps, threads, check=True):
         q = lambda i, f=f, cs=cs: mx.mx_quantize(f, 32, BF, xs[i], rows, cols, cs[i], ss[i], None, st)
         dq = lambda i, f=f, cs=cs: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, BF, ys[i], st)
         if f != 0:  # the E2M3 quantize is the headline
-            S.time(f"quantize_{nm}", q, n, rows * cols * 2, nb * (bpb + 1), note)
+            S.time(f"quantize_{nm}", q, n, rows * cols * 2, nb * (bpb + 1), note,
+                   copy_bpb=(64, bpb + 1))
         S.launch(nm, q)(0)
-        S.time(f"dequantize_{nm}_to_bf16", dq, n, nb * (bpb + 1), rows * cols * 2, note)
+        S.time(f"dequantize_{nm}_to_bf16", dq, n, nb * (bpb + 1), rows * cols * 2, note,
+               copy_bpb=(bpb + 1, 64))
         S.launch(nm, dq)(0)
         torch.cuda.synchronize()
         if check:
@@ -317,12 +365,14 @@ def secondary(mx, steps, threads, check=True):
     xs = bf16_dev(a, n)
     ys = [torch.empty_like(xs[0]) for _ in range(n)]
     fq = lambda i: mx.mx_fake_quantize(4, 32, BF, xs[i], ys[i], rows, cols, st)
-    S.time("fake_quantize_axs6", fq, n, rows * cols * 2, rows * cols * 2, note)
+    S.time("fake_quantize_axs6", fq, n, rows * cols * 2, rows * cols * 2, note,
+           copy_bpb=(64, 64))
     cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
     ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
     aa = [torch.empty((nb + 3) // 4, dtype=torch.uint8, device="cuda") for _ in range(n)]
     q = lambda i: mx.mx_quantize(4, 32, BF, xs[i], rows, cols, cs[i], ss[i], aa[i], st)
-    S.time("quantize_axs6", q, n, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, note)
+    S.time("quantize_axs6", q, n, rows * cols * 2, nb * 24 + nb + (nb + 3) // 4, note,
+           copy_bpb=(64, 25))
     S.launch("fq", fq)(0)
     S.launch("q", q)(0)
     torch.cuda.synchronize()
@@ -366,9 +416,11 @@ def secondary(mx, steps, threads, check=True):
         cs = [torch.empty(nb * bpb, dtype=torch.uint8, device="cuda") for _ in range(n)]
         q = lambda i, f=f, cs=cs: mx.mx_quantize(f, 32, BF, xs[i], rows, cols, cs[i], ss[i], None, st)
         dq = lambda i, f=f, cs=cs: mx.mx_dequantize(f, 32, cs[i], ss[i], None, rows, cols, BF, ys[i], st)
-        S.time(f"quantize_{nm}_activations", q, n, rows * cols * 2, nb * (bpb + 1), note)
+        S.time(f"quantize_{nm}_activations", q, n, rows * cols * 2, nb * (bpb + 1), note,
+               copy_bpb=(64, bpb + 1))
         S.launch(nm, q)(0)
-        S.time(f"dequantize_{nm}_activations", dq, n, nb * (bpb + 1), rows * cols * 2, note)
+        S.time(f"dequantize_{nm}_activations", dq, n, nb * (bpb + 1), rows * cols * 2, note,
+               copy_bpb=(bpb + 1, 64))
         S.launch(nm, dq)(0)
         torch.cuda.synchronize()
         gs = host(ss[0])
@@ -413,7 +465,8 @@ def secondary(mx, steps, threads, check=True):
                  floor_note="same grid, loads and stores with no exp or conversion")
     S.launch("sq", sq)(0)  # the real outputs again, after the floor probe
     dq = lambda i: mx.mx_dequantize(2, 32, c, sc, None, rows, cols, FP, pd, st)
-    S.time("dequantize_e2m1_to_fp32", dq, 1, nb * 17, rows * cols * 4, note, steps=kk, warm=2)
+    S.time("dequantize_e2m1_to_fp32", dq, 1, nb * 17, rows * cols * 4, note, steps=kk, warm=2,
+           copy_bpb=(17, 128))
     torch.cuda.synchronize()
     if check:
         gc, gs, gp = host(c), host(sc), host(pd)

@@ -136,6 +136,47 @@ __device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void
 }
 
 // ---------------------------------------------------------------------------
+// Coalesced input for a wave tile of 64 bf16 blocks (4 KB): four direct
+// global->LDS loads, each covering 1 KB of consecutive bytes, then lane l
+// reads its block's four 16-byte quarters from LDS.  The quarters of block
+// b sit at slots 4b + (q ^ ((b / 4) % 4)): the 16 lanes of one LDS read
+// cycle (blocks 16c..16c+15, one quarter each) then hit 16 distinct slots,
+// and the map is its own inverse, so lane l of load i fetches the piece that
+// slot 64i + l holds.  tile (wave-uniform) must hold 256 slots; it is free
+// for other use once the function returns (every lane has its block in
+// registers).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glob_void_t;
+
+__device__ __forceinline__ int quarter_slot(int b, int q) { return 4 * b + (q ^ ((b >> 2) & 3)); }
+
+__device__ __forceinline__ void load_bf16_tile_coalesced(const void* x, int64_t b0, uint4* tile,
+                                                         int lane, uint32_t (&d)[16]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x) + 4 * b0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int S = 64 * i + lane;
+    __builtin_amdgcn_global_load_lds((glob_void_t*)(src + quarter_slot(S >> 2, S & 3)),
+                                     (lds_void_t*)(tile + 64 * i), 16, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = tile[quarter_slot(lane, q)];
+    d[4 * q] = v.x; d[4 * q + 1] = v.y; d[4 * q + 2] = v.z; d[4 * q + 3] = v.w;
+  }
+  // the caller's stores reuse the tile region only after every lane has
+  // read its block
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
 // MX formats (E2M3, E3M2, E2M1, E4M3): hardware conversions
 // ---------------------------------------------------------------------------
 // Block b of one tensor: scale byte, codes, and both stores.
@@ -195,7 +236,7 @@ __global__ __launch_bounds__(256) void dequantize_mx(const void* __restrict__ co
   constexpr int W = Fmt<F>::W;
   constexpr int NCH = BF16 ? 4 : 8;  // 16-byte output chunks per block
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
@@ -230,14 +271,15 @@ __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t n
   constexpr int W = Fmt<F>::W;
   constexpr int NCH = BF16 ? 4 : 8;
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
     uint32_t o[W];
     uint32_t d[4 * NCH] = {};
     if constexpr (BF16) {
-      if (b < nb) load_bf16_block(x, b, d);
+      if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
+      else if (b < nb) load_bf16_block(x, b, d);
       const uint32_t byte = scale_byte_from_amax<F>(amax_bf16x32(d));
       const float sc = scale_operand(byte);
       encode_bf16<F>(d, sc, o);
@@ -297,15 +339,34 @@ __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     uint32_t v[32], c[32], o[6];
-    load_values<BF16>(x, b, v);
-    const uint32_t byte = axs6_block_byte(v);
-    const int neg_exp = 127 - (int)byte;
+    uint32_t byte;
+    if constexpr (BF16) {
+      uint32_t d[16];
+      load_bf16_block(x, b, d);
+      byte = scale_byte_from_amax<F_AXS6>(amax_bf16x32(d));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[2 * k] = d[k] << 16;
+        v[2 * k + 1] = d[k] & 0xFFFF0000u;
+      }
+    } else {
+      load_values<BF16>(x, b, v);
+      byte = axs6_block_byte(v);
+    }
+    // m = min(rint(16 |v| / X), 31) with 16 |v| / X = |v| 2^(131 - byte)
+    // exactly (as in fake_quantize_axs6); the sign bit is v's
+    const int e_in = 131 - (int)byte;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const Rounded q = round_scaled<F_AXS6>(scaled_abs<F_AXS6>(v[k], neg_exp));
-      c[k] = (byte == 0xFFu) ? 0u : (q.mag | ((v[k] >> 31) << 5));
+      const float m = __builtin_fminf(
+          __builtin_rintf(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(v[k])), e_in)), 31.0f);
+      c[k] = (uint32_t)m | ((v[k] >> 26) & 32u);
     }
     pack32<6>(c, o);
+    if (byte == 0xFFu) {  // rare: a block with a NaN or an infinity has no codes
+#pragma unroll
+      for (int k = 0; k < 6; ++k) o[k] = 0u;
+    }
     store_codes<6>(codes, b, o);
     scales[b] = (uint8_t)byte;
     // config plane: 2 bits per block, all zero (the uniform grid)
@@ -317,28 +378,51 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t nb, void* y) {
   constexpr int NCH = BF16 ? 4 : 8;
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
     uint32_t v[32] = {};
-    if (b < nb) load_values<BF16>(x, b, v);
-    const uint32_t byte = axs6_block_byte(v);
-    const int neg_exp = 127 - (int)byte, sexp = (int)byte - 127;
+    uint32_t byte;
+    if constexpr (BF16) {
+      uint32_t d[16] = {};
+      if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
+      else if (b < nb) load_bf16_block(x, b, d);
+      byte = scale_byte_from_amax<F_AXS6>(amax_bf16x32(d));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[2 * k] = d[k] << 16;
+        v[2 * k + 1] = d[k] & 0xFFFF0000u;
+      }
+    } else {
+      if (b < nb) load_values<BF16>(x, b, v);
+      byte = axs6_block_byte(v);
+    }
+    // the same rounding as quantize_axs6, on signed values: 16 |v| / X =
+    // |v| 2^(131 - byte) exactly (a value small enough to lose bits there
+    // rounds to zero either way), rint is symmetric (so a negative value
+    // that rounds to zero gives -0), and clamping the rounded value to
+    // [-31, 31] equals clamping |v| / X to 31/16 first; the result
+    // m 2^(byte - 131) is exact
+    const int e_in = 131 - (int)byte, e_out = (int)byte - 131;
     uint32_t out[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const Rounded q = round_scaled<F_AXS6>(scaled_abs<F_AXS6>(v[k], neg_exp));
-      const float mag = __builtin_ldexpf(q.val, sexp);  // exact
-      out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(mag) | (v[k] & 0x80000000u));
+      const float m = __builtin_amdgcn_fmed3f(
+          __builtin_rintf(__builtin_ldexpf(__uint_as_float(v[k]), e_in)), -31.0f, 31.0f);
+      out[k] = __float_as_uint(__builtin_ldexpf(m, e_out));
     }
+    const bool poisoned = byte == 0xFFu;  // a block with a NaN or an infinity
     if constexpr (BF16) {
-      // every result is a bf16 value (or the canonical NaN): keep the top half
+      // every result is a bf16 value: keep the top halves
       uint32_t d[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) d[k] = (out[2 * k] >> 16) | (out[2 * k + 1] & 0xFFFF0000u);
+      for (int k = 0; k < 16; ++k)
+        d[k] = poisoned ? kNaN16x2 : __builtin_amdgcn_perm(out[2 * k + 1], out[2 * k], 0x07060302u);
       store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) out[k] = poisoned ? kNaN32 : out[k];
       store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
     }
   }
@@ -351,7 +435,7 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
                                                        void* __restrict__ y) {
   constexpr int NCH = BF16 ? 4 : 8;
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
@@ -492,7 +576,7 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
                                                           ExmyParams p) {
   constexpr int NCH = BF16 ? 4 : 8;
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
@@ -528,7 +612,7 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
                                                        ExmyParams p) {
   constexpr int NCH = BF16 ? 4 : 8;
   __shared__ uint4 lds[4][kTile * (NCH + 1)];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;

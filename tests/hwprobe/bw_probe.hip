@@ -301,3 +301,45 @@ extern "C" int probe_mix_variant(int variant, const void* x, int64_t nb, void* c
   }
   return (int)hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// A copy of arbitrary byte counts per 32-value block, for the floor of any
+// kernel's byte mix: workgroup w reads its 256 blocks' in_bpb bytes each
+// (one contiguous run of 256 in_bpb bytes) and writes 256 out_bpb bytes,
+// every instruction covering 16 bytes per lane of consecutive memory; every
+// loaded word is folded into the stored ones, so the stores wait for all
+// of the workgroup's loads, as in the kernels.  in_bpb and out_bpb must be
+// multiples of 1/16 of a block's bytes such that 256 in_bpb and 256 out_bpb
+// are multiples of 16 (always true for whole bytes).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bytes_copy(const uint4* __restrict__ x, int64_t in_pieces,
+                                                  uint4* __restrict__ y, int64_t out_pieces,
+                                                  int wg_in, int wg_out) {
+  const int t = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  const int64_t i0 = w * wg_in, o0 = w * wg_out;
+  uint4 acc = make_uint4(t, 0, 0, 0);
+  for (int p = t; p < wg_in; p += 256) {
+    if (i0 + p < in_pieces) {
+      const uint4 v = x[i0 + p];
+      acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+    }
+  }
+  for (int p = t; p < wg_out; p += 256) {
+    if (o0 + p < out_pieces) y[o0 + p] = make_uint4(acc.x + p, acc.y, acc.z, acc.w);
+  }
+}
+
+// x: nb * in_bpb bytes, y: nb * out_bpb bytes (rounded up to 16-byte
+// pieces; device memory, 16-byte aligned).  -1 for a bad size.
+extern "C" int probe_bytes_copy(const void* x, int64_t nb, int in_bpb, void* y, int out_bpb,
+                                void* stream) {
+  if (nb < 1 || in_bpb < 1 || out_bpb < 1 || (256 * in_bpb) % 16 || (256 * out_bpb) % 16) return -1;
+  const int64_t g = (nb + 255) / 256;
+  if (g > 0x7FFFFFFF) return -1;
+  const int64_t in_pieces = (nb * in_bpb + 15) / 16, out_pieces = (nb * out_bpb + 15) / 16;
+  hipLaunchKernelGGL(bytes_copy, dim3((unsigned)g), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(x), in_pieces, static_cast<uint4*>(y), out_pieces,
+                     256 * in_bpb / 16, 256 * out_bpb / 16);
+  return (int)hipGetLastError();
+}
