@@ -88,6 +88,8 @@ const char* mx_status_str(mx_status status) {
     case MX_ERR_ALIGN: return "x, y and codes must be 16-byte aligned";
     case MX_ERR_UNSUPPORTED: return "unsupported format, dtype or block size (block must be 32)";
     case MX_ERR_DEVICE: return "HIP kernel launch failed";
+    case MX_ERR_VALUE: return "a scalar argument is outside its range (attention scale: "
+                              "positive, scale * log2(e) finite)";
     default: return "unknown status";
   }
 }
@@ -269,6 +271,10 @@ mx_status attention(bool efq, mx_format v_fmt, int block, const void* q, const v
   if (heads > 0 && lq > 0 && (heads * lq > INT64_MAX / (2 * 128 * 16) ||
                               heads * lk > INT64_MAX / (2 * 128 * 16)))
     return MX_ERR_SHAPE;
+  // the kernel takes the running maximum on the raw scores and scales it
+  // by c = scale * log2(e), which orders the same only for c > 0
+  const float c = scale * 0x1.715476p+0f;
+  if (!(scale > 0.0f) || !(c < INFINITY)) return MX_ERR_VALUE;
   if ((p_codes == nullptr) != (p_scales == nullptr)) return MX_ERR_NULL;
   if (heads == 0 || lq == 0) return MX_OK;
   if (!q || !k || !v_codes || !v_scales || !o) return MX_ERR_NULL;

@@ -14,8 +14,9 @@
 //                            tile's keys in a permuted order, chosen so that
 //                            each lane receives the 32 scores of one
 //                            (query, 32-key block) pair with no exchange
-//   t    = S * scale; tile max; rescale O and l when the maximum grows
-//   p    = exp_ref(t - m); block scale byte; 16 E2M1 codes per lane, which
+//   t    = S * c with c = scale * log2(e) (scores in powers of two); tile
+//          max; rescale O and l when the maximum grows
+//   p    = 2^(t - m) (exp2_ref); block scale byte; 16 E2M1 codes per lane, which
 //          are exactly the lane's B operand of the block-scaled MFMA
 //   O^T += V^T * P^T         4 block-scaled 32x32x64 MFMAs (V in E4M3,
 //                            E2M3, E3M2 or E2M1, P in E2M1)
@@ -38,7 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "mx_exp.h"
+#include "mx_exp2.h"
 #include "mx_formats.h"
 #include "mx_hw.h"
 #include "mx_kernels.h"
@@ -276,7 +277,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
     acc[0][r] = 0.0f; acc[1][r] = 0.0f; acc[2][r] = 0.0f; acc[3][r] = 0.0f;
     lacc[r] = 0.0f;
   }
-  float m = -INFINITY;
+  // running maxima: ms of the raw scores, m = fp32(ms * c) of t (scaling by
+  // c > 0 keeps the order, so m is also the maximum of the fp32(S * c))
+  const float c = scale * 0x1.715476p+0f;
+  float ms = -INFINITY, m = -INFINITY;
   const i32x8_t ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
   // the B operand of the PV products: E2M1 codes in dwords 0..3, the rest
   // unused by FP4 and kept zero across tiles
@@ -336,44 +340,47 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), qf[i], s1, 0,
                                                    0, 0);
     }
-    // every lane holds block h of the tile for its query: x[r] is key
-    // 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4
-    float x[16], y[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * scale;
-      y[r] = s1[r] * scale;
-    }
     const bool dead = !two && h;  // the block past lk of a 32-key last tile
 
-    // Tile maximum with NaN propagation (IEEE maximum): a NaN score, or an
-    // infinite running maximum, sends the whole wave through the careful
-    // path below; otherwise no shifted score can be NaN.
-    float mt = x[0];
+    // Tile maximum of the raw scores with NaN propagation (IEEE maximum): a
+    // NaN score, or a running maximum whose t is infinite, sends the whole
+    // wave through the careful path below; otherwise no shifted score can
+    // be NaN.
+    float mt = s0[0];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mt, x[r]), y[r]);
+      mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mt, s0[r]), s1[r]);
     mt = dead ? -INFINITY : mt;
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
       mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const bool careful = __any(mt != mt || !(__builtin_fabsf(fmaxf(m, mt)) < INFINITY));
+    const bool careful = __any(mt != mt || !(__builtin_fabsf(fmaxf(ms, mt) * c) < INFINITY));
     if (__builtin_expect(careful, 0)) {
       // the maximum the method defines skips NaN scores
-      mt = x[0];
+      mt = s0[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, x[r]), y[r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, s0[r]), s1[r]);
       mt = dead ? -INFINITY : mt;
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float mnew = fmaxf(m, mt);
+    ms = fmaxf(ms, mt);
+    const float mnew = ms * c;
+    // every lane holds block h of the tile for its query: x[r] is key
+    // 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4, in powers of
+    // two
+    float x[16], y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = s0[r] * c;
+      y[r] = s1[r] * c;
+    }
     const bool grow = mnew > m;
     if (__any(grow)) {
-      const float alpha = grow ? exp_ref_nonpos(m - mnew) : 1.0f;
+      const float alpha = grow ? exp2_ref_nonpos(m - mnew) : 1.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         acc[0][r] *= alpha; acc[1][r] *= alpha; acc[2][r] *= alpha; acc[3][r] *= alpha;
@@ -392,8 +399,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[8 * g + e] = __float_as_uint(exp_ref_nonpos<true>(x[4 * g + e] - m));
-            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos<true>(y[4 * g + e] - m));
+            v[8 * g + e] = __float_as_uint(exp2_ref_nonpos<true>(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp2_ref_nonpos<true>(y[4 * g + e] - m));
           }
       } else {
         // no NaN score and a finite maximum: the exp without its clamp,
@@ -402,8 +409,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[8 * g + e] = __float_as_uint(exp_ref_nonpos_unclamped(x[4 * g + e] - m));
-            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos_unclamped(y[4 * g + e] - m));
+            v[8 * g + e] = __float_as_uint(exp2_ref_nonpos_unclamped(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp2_ref_nonpos_unclamped(y[4 * g + e] - m));
           }
       }
       // p >= 0 or NaN, so the bit patterns order as the values and a NaN
@@ -412,14 +419,14 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
 #pragma unroll
       for (int e = 0; e < 32; ++e) amax = max(amax, v[e]);
       if (__builtin_expect(!careful && __any(amax >= 0x7F800000u), 0)) {
-        // a score far below the maximum (or -inf) left the unclamped range:
-        // the clamped exp, for the whole wave
+        // a score of -inf (the only finite-maximum input the unclamped
+        // sequence turns into NaN): the clamped exp2, for the whole wave
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[8 * g + e] = __float_as_uint(exp_ref_nonpos(x[4 * g + e] - m));
-            v[8 * g + 4 + e] = __float_as_uint(exp_ref_nonpos(y[4 * g + e] - m));
+            v[8 * g + e] = __float_as_uint(exp2_ref_nonpos(x[4 * g + e] - m));
+            v[8 * g + 4 + e] = __float_as_uint(exp2_ref_nonpos(y[4 * g + e] - m));
           }
         amax = 0u;
 #pragma unroll
@@ -444,18 +451,18 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
         pk[q] = w;
       }
     } else {
-      // EFQ reading, no exp: u = (t - m) log2 e; the MX scale rule on 2^max u;
+      // EFQ reading, no exp: u = t - m (already in powers of two); the MX
+      // scale rule on 2^max u;
       // code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5)).  A NaN u
       // (NaN score, or inf - inf) poisons the block through the
       // NaN-propagating maximum.
-      const float kLog2e = 0x1.715476p+0f;
       float u[32];
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          u[8 * g + e] = (x[4 * g + e] - m) * kLog2e;
-          u[8 * g + 4 + e] = (y[4 * g + e] - m) * kLog2e;
+          u[8 * g + e] = x[4 * g + e] - m;
+          u[8 * g + 4 + e] = y[4 * g + e] - m;
         }
       float U = u[0];
 #pragma unroll
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
       }
     }
   if (h == 0) {
-    if (row_max) row_max[row] = m;
+    if (row_max) row_max[row] = ms * scale;
     if (row_sum) row_sum[row] = l;
   }
 }

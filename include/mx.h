@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 4
+#define MX_ABI_VERSION 5
 #define MX_BLOCK 32
 
 typedef enum {
@@ -100,7 +100,8 @@ typedef enum {
   MX_ERR_SHAPE = 2,       /* rows/cols negative, or cols % 32 != 0 */
   MX_ERR_ALIGN = 3,       /* x, y or codes not 16-byte aligned */
   MX_ERR_UNSUPPORTED = 4, /* format, dtype or block size not supported */
-  MX_ERR_DEVICE = 5       /* the HIP launch failed */
+  MX_ERR_DEVICE = 5,      /* the HIP launch failed */
+  MX_ERR_VALUE = 6        /* a scalar argument outside its range */
 } mx_status;
 
 /* MX_ABI_VERSION of the built library. */
@@ -191,11 +192,16 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
  * is used for the PV product and for the normalizing sum).  Per head and
  * query row:
  *   s = q . k in fp32 (bf16 products, fp32 matrix-core accumulation),
- *   t = fp32(s * scale);
+ *   t = fp32(s * c) with c = fp32(scale * log2 e): the scaled score in
+ *   powers of two, so that exp(s scale - max) is 2^(t - max t);
  *   keys are taken 64 at a time: m_new = max(m, max t over the tile) (NaN
  *   scores are skipped by the maximum); if m_new > m the running sums are
- *   multiplied by exp(m - m_new); p = exp(t - m_new) with the fp32 exp of
- *   mx_softmax_quantize; p is quantized per 32 keys to E2M1 by the rules
+ *   multiplied by 2^(m - m_new); p = 2^(t - m_new) with a fixed fp32 2^u
+ *   (n = rint(u); the degree-6 polynomial interpolating 2^f at the seven
+ *   Chebyshev points of [-1/2, 1/2], coefficients rounded to fp32, by
+ *   Horner's rule with fused multiply-adds at f = u - n; scaling by 2^n
+ *   with one rounding: within about one ulp of 2^u, exact at integers);
+ *   p is quantized per 32 keys to E2M1 by the rules
  *   above (a NaN p gives a 0xFF block, which makes the row's output NaN);
  *   the numerator adds P * V, the denominator adds P * 1, both from the
  *   decoded E2M1 codes, in fp32;
@@ -210,10 +216,12 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
  *             lk/32, bpb], scales [heads, d, lk/32]
  *   heads, lq, lk, d    d must be 128; lk > 0, a multiple of 32 and at
  *             most 2^24; heads == 0 or lq == 0 is a no-op
- *   scale     score multiplier (typically 1/sqrt(d)), any fp32
+ *   scale     score multiplier (typically 1/sqrt(d)): positive, with
+ *             scale * log2 e finite (MX_ERR_VALUE otherwise)
  *   o         [heads, lq, d] of out_dtype
- *   row_max, row_sum    [heads, lq] fp32: the final m and denominator; may
- *             be NULL
+ *   row_max, row_sum    [heads, lq] fp32: the row's largest fp32(s * scale)
+ *             (NaN scores skipped) and the final denominator (the sum of
+ *             the E2M1 probabilities relative to 2^(max t)); may be NULL
  *   p_codes, p_scales   [heads, lq, lk/32, 16] and [heads, lq, lk/32]: the
  *             E2M1 probability blocks exactly as they entered the PV
  *             product (relative to the running maximum of their tile); both
@@ -234,7 +242,8 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void *q,
  * block normalizes the shifted scores, and a single affine rule turns them
  * into E2M1 codes without a sign).  The page prints no constants; this library's
  * reading, identical in the CPU reference:
- *   u = fp32((t - m_new) * log2 e) for the block's 32 keys,
+ *   u = fp32(t - m_new) for the block's 32 keys (t is already in powers
+ *   of two),
  *   byte = clamp(floor(max u) - 2 + 127, 0, 254) (the MX rule on 2^max u),
  *   code = trunc(clamp(fp32(fma(u - (byte - 127), 2, 2.5)), 0, 7.5)),
  * so shifted scores at exact powers of two land on the even codes that hold

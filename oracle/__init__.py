@@ -74,6 +74,10 @@ def _load():
     lib.mxref_fake_quantize.argtypes = [I, I, I, P, P, I64, I64]
     lib.mxref_exp.argtypes = [ctypes.c_float]
     lib.mxref_exp.restype = ctypes.c_float
+    lib.mxref_exp2.argtypes = [ctypes.c_float]
+    lib.mxref_exp2.restype = ctypes.c_float
+    lib.mxref_exp2_n.argtypes = [P, I64, P]
+    lib.mxref_exp2_n.restype = I
     lib.mxref_softmax_probs.argtypes = [P, I64, I64, P]
     lib.mxref_softmax_quantize.argtypes = [I, I, P, I64, I64, P, P]
     lib.mxref_attention_fwd.argtypes = [I, I, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, I,
@@ -81,9 +85,12 @@ def _load():
     lib.mxref_attention_fwd_efq.argtypes = lib.mxref_attention_fwd.argtypes
     lib.mxref_efq_block.argtypes = [P, P]
     lib.mxref_efq_quantize_block.argtypes = [P, P]
+    lib.mxref_efq_block_log2.argtypes = [P, P]
+    lib.mxref_efq_quantize_block_log2.argtypes = [P, P]
     for f in ("mxref_quantize", "mxref_dequantize", "mxref_fake_quantize",
               "mxref_softmax_probs", "mxref_softmax_quantize", "mxref_attention_fwd",
-              "mxref_attention_fwd_efq", "mxref_efq_block", "mxref_efq_quantize_block"):
+              "mxref_attention_fwd_efq", "mxref_efq_block", "mxref_efq_quantize_block",
+              "mxref_efq_block_log2", "mxref_efq_quantize_block_log2"):
         getattr(lib, f).restype = I
     return lib
 
@@ -182,6 +189,14 @@ def exp_ref(d) -> np.ndarray:
     return out
 
 
+def exp2_ref(u) -> np.ndarray:
+    """The attention forward's fixed base-2 exponential, elementwise (fp32)."""
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    out = np.empty_like(u)
+    _lib.mxref_exp2_n(_ptr(u), u.size, _ptr(out))
+    return out
+
+
 def softmax_probs(s: np.ndarray) -> np.ndarray:
     s = np.ascontiguousarray(s, dtype=np.float32)
     rows, cols = _rows_cols(s)
@@ -220,14 +235,34 @@ def efq_quantize_block(d) -> tuple:
     return byte, packed
 
 
+def efq_block_log2(u) -> tuple:
+    """EFQ reading on 32 shifted scores already in powers of two (the
+    attention forward's t - m): (scale byte, codes[32])."""
+    u = np.ascontiguousarray(np.asarray(u, np.float32).reshape(BLOCK))
+    codes = np.zeros(BLOCK, np.int32)
+    byte = _lib.mxref_efq_block_log2(_ptr(u), _ptr(codes))
+    return byte, codes
+
+
+def efq_quantize_block_log2(u) -> tuple:
+    """The same, packed: (scale byte, 16 packed bytes)."""
+    u = np.ascontiguousarray(np.asarray(u, np.float32).reshape(BLOCK))
+    packed = np.zeros(16, np.uint8)
+    byte = _lib.mxref_efq_quantize_block_log2(_ptr(u), _ptr(packed))
+    return byte, packed
+
+
 def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,
                   v_scales: np.ndarray, scale: float, kv_tile: int = 64, out_dtype: int = FP32,
                   efq: bool = False):
     """Attention forward with E2M1 probabilities (online softmax over
     `kv_tile` keys at a time); efq=True uses the exp-free EFQ reading for the
-    probability blocks instead of exp-then-quantize.  q [heads, lq, d] and k [heads, lk, d] are
-    bf16 bit patterns; v_codes/v_scales are V^T ([heads, d, lk]) quantized
-    with ``quantize(v_fmt, .)``.  Returns (o [heads, lq, d], row_max,
+    probability blocks instead of exp-then-quantize.  Probabilities are
+    evaluated in base 2: t = fp32(s * fp32(scale * log2 e)), p =
+    exp2_ref(t - m) with m the running maximum of t.  q [heads, lq, d] and
+    k [heads, lk, d] are bf16 bit patterns; v_codes/v_scales are V^T
+    ([heads, d, lk]) quantized with ``quantize(v_fmt, .)``.  Returns
+    (o [heads, lq, d], row_max (the largest fp32(s * scale) of the row),
     row_sum [heads, lq], p_codes [heads, lq, lk/32, 16], p_scales
     [heads, lq, lk/32])."""
     q = np.ascontiguousarray(q, dtype=np.uint16)

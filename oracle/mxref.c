@@ -19,8 +19,9 @@
  * Parity pins: format tables, scale rule, RNE/saturation, packing and
  * dequantization are pinned by the CPU tests (library dtypes, brute-force
  * nearest-code search, closed-form invariants); the eXmY grids by field
- * enumeration, library dtypes and closed forms; the fixed exp by a
- * reference exponential within its error bound; the attention forward by
+ * enumeration, library dtypes and closed forms; the fixed exp and exp2 by
+ * reference exponentials within their error bounds (and exp2's
+ * coefficients by their definition); the attention forward by
  * closed forms (equal scores, a dominant key), brute-force probability
  * blocks and an error bound against exact attention.  The NaN/inf block
  * rule, the bit order inside a packed block and the AXS-6 element/config
@@ -443,6 +444,49 @@ float mxref_exp(float d) {
   return p * ldexpf(1.0f, n);
 }
 
+/* 2^u, for the attention forward's probabilities (attention_fwd below
+ * evaluates exp(t - m) as 2^((t - m) log2 e) with log2 e joined to the
+ * score scale):
+ *   n = rint(u),  f = u - n (exact, |f| <= 1/2),
+ *   p = c0 + c1 f + ... + c6 f^6 by Horner's rule with fused multiply-adds,
+ *   2^u = p * 2^n with one rounding (exact multiplications by powers of two
+ *   as in mxref_exp).
+ * c0..c6 are the coefficients of the degree-6 polynomial interpolating 2^f
+ * at the seven Chebyshev points cos((2k+1) pi / 14) / 2 of [-1/2, 1/2],
+ * each rounded to fp32; one of the points is f = 0, so c0 = 1 exactly and
+ * 2^u is exact for every integer u in [-149, 0]. */
+float mxref_exp2(float u) {
+  const float C0 = 0x1.000000p+0f, C1 = 0x1.62e430p-1f, C2 = 0x1.ebfbe0p-3f,
+              C3 = 0x1.c6aeccp-5f, C4 = 0x1.3b2a1cp-7f, C5 = 0x1.5f48c0p-10f,
+              C6 = 0x1.444000p-13f;
+  float nf, f, p;
+  int n;
+  if (isnan(u)) return u;
+  if (u > 128.0f) return INFINITY;
+  if (u < -151.0f) return 0.0f;
+  nf = rintf(u);
+  f = u - nf;
+  p = C6;
+  p = fmaf(p, f, C5);
+  p = fmaf(p, f, C4);
+  p = fmaf(p, f, C3);
+  p = fmaf(p, f, C2);
+  p = fmaf(p, f, C1);
+  p = fmaf(p, f, C0);
+  n = (int)nf;
+  if (n < -100) { p = p * 0x1p-50f; n += 50; }
+  if (n > 100) { p = p * 0x1p+50f; n -= 50; }
+  return p * ldexpf(1.0f, n);
+}
+
+/* mxref_exp2 over an array (for the tests' dense sweeps) */
+int mxref_exp2_n(const float *u, int64_t n, float *out) {
+  int64_t i;
+  if (n < 0) return -1;
+  for (i = 0; i < n; i++) out[i] = mxref_exp2(u[i]);
+  return 0;
+}
+
 /* P = exp(s - rowmax) per row.  The row maximum is exact; a NaN anywhere
  * in the row makes it NaN.  d = s - rowmax is one fp32 subtraction. */
 int mxref_softmax_probs(const float *s, int64_t rows, int64_t cols, float *p) {
@@ -511,12 +555,15 @@ int mxref_softmax_quantize(int fmt, int block, const float *s, int64_t rows,
 /* leaves this open; reading: the same operand, as in the EFQ path).   */
 /* Readings where the pages are silent:                                */
 /*  - scores s = q . k from bf16 q, k, summed in double and rounded     */
-/*    once to fp32; t = fp32(s * scale);                               */
-/*  - the running maximum is updated once per kv_tile keys (NaN scores */
-/*    are skipped by the maximum, as fmax does); alpha =               */
-/*    exp_ref(m_old - m_new) rescales the sums only when m grows;      */
-/*  - p = exp_ref(fp32(t - m_new)), quantized per 32 keys to E2M1 by   */
-/*    the MX rules above (a NaN p poisons its block, so the row's       */
+/*    once to fp32;                                                     */
+/*  - exp is evaluated in base 2: c = fp32(scale * log2 e) and          */
+/*    t = fp32(s * c), the scaled score in powers of two, so that       */
+/*    exp(s scale - max) = 2^(t - max t) (rounding aside);              */
+/*  - the running maximum of t is updated once per kv_tile keys (NaN   */
+/*    scores are skipped by the maximum, as fmax does); alpha =        */
+/*    mxref_exp2(m_old - m_new) rescales the sums only when m grows;   */
+/*  - p = mxref_exp2(fp32(t - m_new)), quantized per 32 keys to E2M1   */
+/*    by the MX rules above (a NaN p poisons its block, so the row's    */
 /*    output is NaN);                                                   */
 /*  - V arrives transposed and block-quantized along the keys (V^T as  */
 /*    [d, lk] in any MX element format), and is decoded exactly;        */
@@ -524,7 +571,8 @@ int mxref_softmax_quantize(int fmt, int block, const float *s, int64_t rows,
 /*    E2M1 values; o = numerator / l, rounded once to the output type. */
 /* Layouts: q [heads, lq, d], k [heads, lk, d] (bf16 bits); v_codes    */
 /* [heads, d, lk/32, bpb], v_scales [heads, d, lk/32]; o [heads, lq,   */
-/* d]; row_max, row_sum [heads, lq] (the final m and fp32(l));         */
+/* d]; row_max, row_sum [heads, lq] (the row's largest fp32(s * scale) */
+/* in natural units, NaN scores skipped, and fp32(l));                  */
 /* p_codes [heads, lq, lk/32, 16], p_scales [heads, lq, lk/32]: the    */
 /* E2M1 blocks as they entered the PV product.  The last four may be   */
 /* NULL.                                                                */
@@ -545,6 +593,8 @@ static double bf16_value(uint16_t b) {
 /* (PARITY UNPINNED by the pages; only its stated properties are       */
 /* tested):                                                             */
 /*   u = fp32(d * log2 e)             shifted score in powers of two    */
+/*                                    (the attention forward hands in   */
+/*                                    its base-2 t - m directly)        */
 /*   U = max u; byte = clamp(floor(U) - 2 + 127, 0, 254)                */
 /*                                    (the MX rule applied to 2^U)      */
 /*   w = u - (byte - 127)             exact in fp32                     */
@@ -554,19 +604,16 @@ static double bf16_value(uint16_t b) {
 /* midpoints.  A NaN shifted score poisons the block (0xFF, codes 0);   */
 /* U = -inf gives byte 0 and codes 0.                                   */
 /* ------------------------------------------------------------------ */
-int mxref_efq_block(const float *dv, int *codes) {
-  const float LOG2E = 0x1.715476p+0f;
-  float u[BLOCK], U = -INFINITY;
+int mxref_efq_block_log2(const float *u, int *codes) {
+  float U = -INFINITY;
   int k, byte, E;
   for (k = 0; k < BLOCK; k++)
-    if (isnan(dv[k])) {
+    if (isnan(u[k])) {
       for (k = 0; k < BLOCK; k++) codes[k] = 0;
       return 0xFF;
     }
-  for (k = 0; k < BLOCK; k++) {
-    u[k] = dv[k] * LOG2E;
+  for (k = 0; k < BLOCK; k++)
     if (u[k] > U) U = u[k];
-  }
   if (U == -INFINITY) {
     for (k = 0; k < BLOCK; k++) codes[k] = 0;
     return 0;
@@ -585,13 +632,29 @@ int mxref_efq_block(const float *dv, int *codes) {
   return byte;
 }
 
-int mxref_efq_quantize_block(const float *dv, uint8_t *packed) {
+int mxref_efq_block(const float *dv, int *codes) {
+  const float LOG2E = 0x1.715476p+0f;
+  float u[BLOCK];
+  int k;
+  for (k = 0; k < BLOCK; k++) u[k] = dv[k] * LOG2E;
+  return mxref_efq_block_log2(u, codes);
+}
+
+int mxref_efq_quantize_block_log2(const float *u, uint8_t *packed) {
   fmt_t fp;
   int codes[BLOCK], byte;
   get_fmt(MXREF_FP4_E2M1, &fp);
-  byte = mxref_efq_block(dv, codes);
+  byte = mxref_efq_block_log2(u, codes);
   pack_block(&fp, codes, packed);
   return byte;
+}
+
+int mxref_efq_quantize_block(const float *dv, uint8_t *packed) {
+  const float LOG2E = 0x1.715476p+0f;
+  float u[BLOCK];
+  int k;
+  for (k = 0; k < BLOCK; k++) u[k] = dv[k] * LOG2E;
+  return mxref_efq_quantize_block_log2(u, packed);
 }
 
 static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
@@ -600,8 +663,10 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
                          int64_t lk, int64_t d, float scale, int kv_tile,
                          int out_dtype, void *o, float *row_max,
                          float *row_sum, uint8_t *p_codes, uint8_t *p_scales) {
+  const float LOG2E = 0x1.715476p+0f;
   fmt_t fv, fp;
   int64_t h, i, j, c, kk, nbk;
+  float c2;
   double *vhat = 0, *acc = 0;
   float *t = 0;
   if (!get_fmt(v_fmt, &fv) || v_fmt == MXREF_AXS6 || (v_fmt & ~0xFF)) return -1;
@@ -609,6 +674,9 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
   if (block != BLOCK || heads < 0 || lq < 0 || d <= 0 || lk <= 0 ||
       lk % BLOCK || kv_tile <= 0 || kv_tile % BLOCK)
     return -1;
+  /* the scale must be positive with scale * log2 e finite */
+  c2 = scale * LOG2E;
+  if (!(scale > 0.0f) || !(c2 < INFINITY)) return -1;
   nbk = lk / BLOCK;
   vhat = (double *)malloc(sizeof(double) * (size_t)(d * lk));
   acc = (double *)malloc(sizeof(double) * (size_t)d);
@@ -632,15 +700,17 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
       }
     for (i = 0; i < lq; i++) {
       const uint16_t *qi = q + (h * lq + i) * d;
-      float m = -INFINITY;
+      float m = -INFINITY, row_top = -INFINITY;
       double l = 0.0;
       int64_t row = h * lq + i;
-      /* scores of the whole row, t = fp32(fp32(q . k) * scale) */
+      /* scores of the whole row in powers of two, t = fp32(fp32(q . k) * c2),
+       * and the largest fp32(fp32(q . k) * scale) */
       for (kk = 0; kk < lk; kk++) {
         const uint16_t *kr = k + (h * lk + kk) * d;
         double s = 0.0;
         for (c = 0; c < d; c++) s += bf16_value(qi[c]) * bf16_value(kr[c]);
-        t[kk] = (float)s * scale;
+        t[kk] = (float)s * c2;
+        if ((float)s * scale > row_top) row_top = (float)s * scale;
       }
       for (c = 0; c < d; c++) acc[c] = 0.0;
       for (j = 0; j < lk; j += kv_tile) {
@@ -649,7 +719,7 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
         for (kk = j; kk < end; kk++)
           if (t[kk] > m_new) m_new = t[kk]; /* NaN never compares greater */
         if (m_new > m) {
-          double alpha = (double)mxref_exp(m - m_new);
+          double alpha = (double)mxref_exp2(m - m_new);
           l *= alpha;
           for (c = 0; c < d; c++) acc[c] *= alpha;
           m = m_new;
@@ -660,10 +730,10 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
           int codes[BLOCK], e, byte;
           for (e = 0; e < BLOCK; e++) dv[e] = t[kk + e] - m;
           if (rule == 0) {
-            for (e = 0; e < BLOCK; e++) pv[e] = (double)mxref_exp(dv[e]);
+            for (e = 0; e < BLOCK; e++) pv[e] = (double)mxref_exp2(dv[e]);
             byte = quantize_values(&fp, MXREF_FP4_E2M1, pv, codes);
           } else {
-            byte = mxref_efq_block(dv, codes);
+            byte = mxref_efq_block_log2(dv, codes);
           }
           for (e = 0; e < BLOCK; e++)
             phat[e] = byte == 0xFF ? NAN
@@ -678,7 +748,7 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
         }
       }
       for (c = 0; c < d; c++) store_value(out_dtype, o, row * d + c, acc[c] / l);
-      if (row_max) row_max[row] = m;
+      if (row_max) row_max[row] = row_top;
       if (row_sum) row_sum[row] = (float)l;
     }
   }

@@ -56,6 +56,8 @@ int mxref_fake_quantize(int fmt, int block, int dtype, const void *x, void *y,
 
 /* exp-then-quantize attention probabilities */
 float mxref_exp(float d);
+float mxref_exp2(float u);
+int   mxref_exp2_n(const float *u, int64_t n, float *out);
 int   mxref_softmax_probs(const float *s, int64_t rows, int64_t cols,
                           float *p);
 int   mxref_softmax_quantize(int fmt, int block, const float *s,
@@ -63,8 +65,9 @@ int   mxref_softmax_quantize(int fmt, int block, const float *s,
                              uint8_t *codes, uint8_t *scales);
 
 /* attention forward: online softmax over kv_tile keys at a time, exp
- * then E2M1 quantization of the probabilities, V^T block-quantized along
- * the keys (layouts next to the definition in mxref.c) */
+ * (in base 2, mxref_exp2) then E2M1 quantization of the probabilities, V^T
+ * block-quantized along the keys (layouts next to the definition in
+ * mxref.c) */
 int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
                         const uint16_t *k, const uint8_t *v_codes,
                         const uint8_t *v_scales, int64_t heads, int64_t lq,
@@ -76,6 +79,9 @@ int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
  * the E2M1 codes of one block of 32 shifted scores, and the scale byte */
 int mxref_efq_block(const float *dv, int *codes);
 int mxref_efq_quantize_block(const float *dv, uint8_t *packed);
+/* the same on shifted scores already in powers of two (u = d log2 e) */
+int mxref_efq_block_log2(const float *u, int *codes);
+int mxref_efq_quantize_block_log2(const float *u, uint8_t *packed);
 int mxref_attention_fwd_efq(int v_fmt, int block, const uint16_t *q,
                             const uint16_t *k, const uint8_t *v_codes,
                             const uint8_t *v_scales, int64_t heads,

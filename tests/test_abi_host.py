@@ -51,8 +51,8 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 4
-    for s in range(0, 7):
+    assert mx.mx_abi_version() == 5
+    for s in range(0, 8):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
 
@@ -204,15 +204,15 @@ def test_generic_exmy_formats_host_checks(mx):
 
 def test_attention_argument_errors(mx):
     A = 1 << 20  # a fake 16-byte-aligned address; nothing is launched
-    OK, NULL, SHAPE, ALIGN, UNSUP = 0, 1, 2, 3, 4
+    OK, NULL, SHAPE, ALIGN, UNSUP, VALUE = 0, 1, 2, 3, 4, 6
     E4M3, E2M3, E3M2, E2M1, AXS6 = mx.MX_FP8_E4M3, mx.MX_FP6_E2M3, mx.MX_FP6_E3M2, \
         mx.MX_FP4_E2M1, mx.MX_AXS6
 
     def call(v_fmt=E4M3, block=32, q=A, k=A, vc=A, vs=A, heads=2, lq=64, lk=128, d=128,
-             out=mx.MX_BF16, o=A, pc=None, ps=None):
-        rc = mx.mx_attention_fwd(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out, o,
+             out=mx.MX_BF16, o=A, pc=None, ps=None, scale=0.125):
+        rc = mx.mx_attention_fwd(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, scale, out, o,
                                  None, None, pc, ps, stream=0)
-        rc_efq = mx.mx_attention_fwd_efq(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, 0.125, out,
+        rc_efq = mx.mx_attention_fwd_efq(v_fmt, block, q, k, vc, vs, heads, lq, lk, d, scale, out,
                                          o, None, None, pc, ps, stream=0)
         assert rc == rc_efq
         return rc
@@ -227,6 +227,13 @@ def test_attention_argument_errors(mx):
     assert call(lk=(1 << 24) + 32) == SHAPE
     assert call(lq=-1) == SHAPE
     assert call(heads=-1) == SHAPE
+    # the scale must be positive with scale * log2(e) finite (the kernel
+    # orders the scores before scaling them)
+    for bad in (0.0, -0.0, -0.125, float("nan"), float("inf"), 3e38):
+        assert call(scale=bad) == VALUE, bad
+        assert call(scale=bad, heads=0) == VALUE, bad
+    assert call(scale=2e38, q=None) == NULL  # 2e38 log2(e) is still finite
+    assert call(scale=1e-45, q=None) == NULL
     assert call(pc=A) == NULL           # probability codes without their scales
     assert call(q=None) == NULL
     assert call(vs=None) == NULL

@@ -7,9 +7,10 @@ by the *oracle* (its codes are uploaded; nothing expected comes from the
 GPU).  Two kinds of scores:
 * exact: q and k hold multiples of 1/4 in [-3, 3], so every product and
   partial sum of q . k (d = 128) is exact in fp32 whatever the
-  accumulation order; t = fp32(s * scale) is then the same number on both
-  sides, and the probability blocks, the scale bytes and the row maxima
-  must agree bit for bit;
+  accumulation order; the scores in powers of two, t = fp32(s *
+  fp32(scale * log2 e)), are then the same numbers on both sides, and the
+  probability blocks, the scale bytes and the row maxima must agree bit
+  for bit;
 * natural: bf16 N(0, 1) q and k; the fp32 matrix-core sum may differ from
   the oracle's correctly rounded score in the last bits, which can move a
   probability across an E2M1 rounding boundary; such blocks are counted

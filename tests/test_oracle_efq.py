@@ -4,7 +4,9 @@ The EFQ explainer says what the rule does (an exponent-only block scale
 taken from the largest value in the block, then one affine map from shifted scores to
 nonnegative E2M1 codes, no exp) but prints no constants, so the oracle
 implements a stated reading: u = fp32(d log2 e), byte = the MX rule on 2^U
-(U = max u), w = u - (byte - 127), code = trunc(clamp(2w + 2.5, 0, 7.5)).
+(U = max u), w = u - (byte - 127), code = trunc(clamp(2w + 2.5, 0, 7.5)); the
+attention forward, whose scores are already in powers of two, hands in
+u = t - m directly (efq_block_log2).
 PARITY UNPINNED by the pages: these tests pin the reading's own properties
 (exact powers of two land on the even codes, monotonicity, the block
 maximum's code, the log-domain rounding bound, agreement with
@@ -163,13 +165,14 @@ def test_attention_blocks_follow_the_block_rule():
     o, m, l, pc, ps = oracle.attention_fwd(oracle.FP8_E4M3, q, k, vc, vs, scale, efq=True)
     s = np.einsum("hqd,hkd->hqk", workloads.bf16_bits_to_f32(q).astype(np.float64),
                   workloads.bf16_bits_to_f32(k).astype(np.float64)).astype(np.float32)
-    t = (s * scale).astype(np.float32)
+    # the forward's scores in powers of two: t = fp32(s * fp32(scale * log2 e))
+    t = (s * np.float32(scale * LOG2E)).astype(np.float32)
     for h in range(heads):
         for i in range(lq):
             run_max = np.float32(-np.inf)
             for j in range(0, lk, 64):
                 run_max = max(run_max, t[h, i, j:j + 64].max())
                 for b in range(j, min(j + 64, lk), 32):
-                    byte, packed = oracle.efq_quantize_block((t[h, i, b:b + 32] - run_max)
-                                                             .astype(np.float32))
+                    byte, packed = oracle.efq_quantize_block_log2((t[h, i, b:b + 32] - run_max)
+                                                                  .astype(np.float32))
                     assert ps[h, i, b // 32] == byte and pc[h, i, b // 32].tobytes() == packed.tobytes()

@@ -8,6 +8,7 @@ oracle/mxref.c fails at least one of them.
 import json
 import math
 import os
+import re
 
 import numpy as np
 import pytest
@@ -525,6 +526,77 @@ def test_exp_ref_subnormal_range_and_monotone():
     dd = np.sort(np.concatenate([d, np.linspace(-30, 0, 300001).astype(np.float32)]))
     pp = _exp_many(dd)
     assert np.all(np.diff(pp.astype(np.float64)) >= 0)
+
+
+# ----------------------------------------------------------------------------
+# (g2) the attention forward's base-2 exponential
+# ----------------------------------------------------------------------------
+def _exp2_literals():
+    """The coefficients C0..C6 as written in mxref_exp2's source."""
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "mxref.c")).read()
+    body = src[src.index("float mxref_exp2(float u)"):]
+    body = body[:body.index("float nf")]
+    return {int(j): float.fromhex(v)
+            for j, v in re.findall(r"C(\d) = (0x[0-9a-f.]+p[+-]\d+)f", body)}
+
+
+def test_exp2_coefficients_are_the_chebyshev_interpolant():
+    # the stated definition, computed here in float64: the degree-6
+    # polynomial through 2^x at the Chebyshev points cos((2k+1) pi/14)/2
+    n = 7
+    x = np.cos((2 * np.arange(n) + 1) * np.pi / (2 * n)) / 2
+    c = np.linalg.solve(np.vander(x, n, increasing=True), np.exp2(x))
+    lit = _exp2_literals()
+    assert sorted(lit) == list(range(n))
+    assert [np.float32(c[j]) for j in range(n)] == [np.float32(lit[j]) for j in range(n)]
+    assert lit[0] == 1.0 and abs(c[0] - 1.0) < 1e-15  # the node x = 0
+
+
+def _ulps(p, ref):
+    # error in units of the last place of the exact value's binade (normal
+    # range); one subnormal ulp 2^-149 below 2^-126
+    _, e = np.frexp(ref)
+    ulp = np.maximum(np.ldexp(1.0, e - 24), 2.0 ** -149)
+    return np.abs(p - ref) / ulp
+
+
+def test_exp2_ref_within_one_ulp():
+    # (over every fp32 f in [-1/2, 1/2], the whole reduced range, the
+    # largest error is 0.992 ulp; the scaling by 2^n keeps the count)
+    rng = np.random.default_rng(21)
+    u = np.concatenate([np.linspace(-0.5, 0.5, 400001), rng.uniform(-0.5, 0.5, 300000),
+                        rng.uniform(-151.0, 0.0, 300000), -rng.exponential(4.0, 100000)])
+    u = u.astype(np.float32)
+    err = _ulps(oracle.exp2_ref(u).astype(np.float64), np.exp2(u.astype(np.float64)))
+    assert err.max() <= 1.0, err.max()
+    assert np.mean(err <= 0.5) > 0.9
+
+
+def test_exp2_ref_special_values():
+    k = np.arange(150, dtype=np.float32)
+    # exact powers of two down to the smallest subnormal
+    assert np.array_equal(oracle.exp2_ref(-k), np.exp2(-k.astype(np.float64)).astype(np.float32))
+    # 2^-150 is the midpoint between 0 and 2^-149 (ties to even: 0); below
+    # it everything is 0, and just above it the result is 2^-149
+    zero = np.array([-150.0, -150.5, -151.0, -151.5, -1e6, -3e38, -np.inf], np.float32)
+    assert np.all(oracle.exp2_ref(zero) == 0.0)
+    assert oracle.exp2_ref(np.nextafter(np.float32(-150.0), np.float32(0.0)))[0] == 2.0 ** -149
+    assert np.isnan(oracle.exp2_ref(np.array([np.nan], np.float32))[0])
+    assert np.isinf(oracle.exp2_ref(np.array([128.5], np.float32))[0])
+
+
+def test_exp2_ref_agrees_with_exp_ref_in_base_e():
+    # exp_ref(d) and exp2_ref(fp32(d log2 e)) evaluate the same function;
+    # they differ by the roundings of log2 e and of d log2 e (together
+    # <= |u| 2^-23 in the exponent, a relative ln2 |u| 2^-23) plus an ulp
+    # or two
+    rng = np.random.default_rng(22)
+    d = -np.abs(rng.standard_normal(200000) * 8).astype(np.float32)
+    u = (d * np.float32(1.4426950408889634)).astype(np.float32)
+    a = oracle.exp2_ref(u).astype(np.float64)
+    b = _exp_many(d).astype(np.float64)
+    rel = np.abs(a - b) / b
+    assert np.all(rel <= np.log(2) * np.abs(u) * 2.0 ** -23 + 4 * 2.0 ** -24)
 
 
 def test_softmax_quantize_structure():
