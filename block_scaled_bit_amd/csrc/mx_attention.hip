@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       mt = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mt, s0[r]), s1[r]);
+    const float bmax = mt;  // the lane's block, NaN if any of its scores is
     mt = dead ? -INFINITY : mt;
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
@@ -369,15 +370,6 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
     }
     ms = fmaxf(ms, mt);
     const float mnew = ms * c;
-    // every lane holds block h of the tile for its query: x[r] is key
-    // 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4, in powers of
-    // two
-    float x[16], y[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * c;
-      y[r] = s1[r] * c;
-    }
     const bool grow = mnew > m;
     if (__any(grow)) {
       const float alpha = grow ? exp2_ref_nonpos(m - mnew) : 1.0f;
@@ -392,6 +384,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
     uint32_t byte;
     uint32_t pk[Fmt<F_E2M1>::W];
     if constexpr (!EFQ) {
+      // every lane holds block h of the tile for its query: x[r] is key
+      // 8(r/4) + r%4 of the block, y[r] is key 8(r/4) + 4 + r%4, in powers
+      // of two
+      float x[16], y[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = s0[r] * c;
+        y[r] = s1[r] * c;
+      }
       // probabilities of the lane's 32-key block, in key order
       uint32_t v[32];
       if (careful) {
@@ -451,34 +452,28 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_mx(
         pk[q] = w;
       }
     } else {
-      // EFQ reading, no exp: u = t - m (already in powers of two); the MX
-      // scale rule on 2^max u;
-      // code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5)).  A NaN u
-      // (NaN score, or inf - inf) poisons the block through the
-      // NaN-propagating maximum.
-      float u[32];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u[8 * g + e] = x[4 * g + e] - m;
-          u[8 * g + 4 + e] = y[4 * g + e] - m;
-        }
-      float U = u[0];
-#pragma unroll
-      for (int e = 1; e < 32; ++e) U = __builtin_elementwise_maximum(U, u[e]);
+      // EFQ reading, no exp, on u = t - m (already in powers of two): the
+      // MX scale rule on 2^max u, and
+      //   code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5))
+      // with the affine map taken from the raw score in one fused
+      // multiply-add, a = fma(S, 2c, fp32((2.5 - 2 (byte - 127)) - 2m)).
+      // max u = fp32(fp32(bmax c) - m) (both steps keep the order), NaN if
+      // any u is (NaN score, or inf - inf), which poisons the block.
+      const float U = bmax * c - m;
       // floor of max(U, -1000): every U below gives byte 0 as well
       const int E = (int)__builtin_floorf(__builtin_fmaxf(U, -1000.0f));
       const int b = min(max(E - Fmt<F_E2M1>::EMAX + 127, 0), 254);
       const float shift = (float)(b - 127);
+      const float c2 = 2.0f * c;
+      const float k2 = (2.5f - 2.0f * shift) - 2.0f * m;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t w = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float c = __builtin_amdgcn_fmed3f(__builtin_fmaf(u[8 * j + e] - shift, 2.0f, 2.5f),
-                                                  0.0f, 7.5f);
-          w |= (uint32_t)c << (4 * e);
+          const float sv = e < 4 ? s0[4 * j + e] : s1[4 * j + e - 4];
+          const float cd = __builtin_amdgcn_fmed3f(__builtin_fmaf(sv, c2, k2), 0.0f, 7.5f);
+          w |= (uint32_t)cd << (4 * e);
         }
         pk[j] = w;
       }

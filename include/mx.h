@@ -245,7 +245,9 @@ mx_status mx_attention_fwd(mx_format v_fmt, int block, const void *q,
  *   u = fp32(t - m_new) for the block's 32 keys (t is already in powers
  *   of two),
  *   byte = clamp(floor(max u) - 2 + 127, 0, 254) (the MX rule on 2^max u),
- *   code = trunc(clamp(fp32(fma(u - (byte - 127), 2, 2.5)), 0, 7.5)),
+ *   code = trunc(clamp(2 (u - (byte - 127)) + 2.5, 0, 7.5)), the affine map
+ *   evaluated from the raw score as fp32(fma(s, 2c, fp32((2.5 - 2 (byte -
+ *   127)) - 2 m_new))),
  * so shifted scores at exact powers of two land on the even codes that hold
  * those values; a NaN u gives a 0xFF block.  Everything else, arguments and
  * errors included, is as in mx_attention_fwd. */

@@ -87,10 +87,12 @@ def _load():
     lib.mxref_efq_quantize_block.argtypes = [P, P]
     lib.mxref_efq_block_log2.argtypes = [P, P]
     lib.mxref_efq_quantize_block_log2.argtypes = [P, P]
+    lib.mxref_efq_attention_block.argtypes = [P, ctypes.c_float, ctypes.c_float, P]
     for f in ("mxref_quantize", "mxref_dequantize", "mxref_fake_quantize",
               "mxref_softmax_probs", "mxref_softmax_quantize", "mxref_attention_fwd",
               "mxref_attention_fwd_efq", "mxref_efq_block", "mxref_efq_quantize_block",
-              "mxref_efq_block_log2", "mxref_efq_quantize_block_log2"):
+              "mxref_efq_block_log2", "mxref_efq_quantize_block_log2",
+              "mxref_efq_attention_block"):
         getattr(lib, f).restype = I
     return lib
 
@@ -250,6 +252,16 @@ def efq_quantize_block_log2(u) -> tuple:
     packed = np.zeros(16, np.uint8)
     byte = _lib.mxref_efq_quantize_block_log2(_ptr(u), _ptr(packed))
     return byte, packed
+
+
+def efq_attention_block(s, c: float, m: float) -> tuple:
+    """EFQ in the attention forward's form on 32 raw fp32 scores s, with
+    c = fp32(scale * log2 e) and the running maximum m of fp32(s * c):
+    (scale byte, codes[32])."""
+    s = np.ascontiguousarray(np.asarray(s, np.float32).reshape(BLOCK))
+    codes = np.zeros(BLOCK, np.int32)
+    byte = _lib.mxref_efq_attention_block(_ptr(s), float(c), float(m), _ptr(codes))
+    return byte, codes
 
 
 def attention_fwd(v_fmt: int, q: np.ndarray, k: np.ndarray, v_codes: np.ndarray,

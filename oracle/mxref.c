@@ -618,7 +618,8 @@ int mxref_efq_block_log2(const float *u, int *codes) {
     for (k = 0; k < BLOCK; k++) codes[k] = 0;
     return 0;
   }
-  E = (int)floorf(U);
+  /* every U below -1000 gives byte 0 too (and keeps floor in int range) */
+  E = (int)floorf(U < -1000.0f ? -1000.0f : U);
   byte = E - 2 + 127;
   if (byte < 0) byte = 0;
   if (byte > 254) byte = 254;
@@ -628,6 +629,42 @@ int mxref_efq_block_log2(const float *u, int *codes) {
     if (!(x > 0.0f)) x = 0.0f;
     if (x > 7.5f) x = 7.5f;
     codes[k] = (int)x;
+  }
+  return byte;
+}
+
+/* EFQ inside the attention forward: the scale byte as in
+ * mxref_efq_block_log2 from u = fp32(fp32(s c) - m), and the affine map
+ * 2 (u - (byte - 127)) + 2.5 evaluated from the raw fp32 score s in one
+ * fused multiply-add, a = fma(s, 2c, fp32((2.5 - 2 (byte - 127)) - 2m))
+ * (the same exact value before rounding, with fewer roundings);
+ * code = trunc(clamp(a, 0, 7.5)). */
+int mxref_efq_attention_block(const float *s, float c, float m, int *codes) {
+  float u[BLOCK], U = -INFINITY, k2, a;
+  int k, byte, E;
+  for (k = 0; k < BLOCK; k++) {
+    u[k] = s[k] * c - m;
+    if (isnan(u[k])) {
+      for (k = 0; k < BLOCK; k++) codes[k] = 0;
+      return 0xFF;
+    }
+  }
+  for (k = 0; k < BLOCK; k++)
+    if (u[k] > U) U = u[k];
+  if (U == -INFINITY) {
+    for (k = 0; k < BLOCK; k++) codes[k] = 0;
+    return 0;
+  }
+  E = (int)floorf(U < -1000.0f ? -1000.0f : U);
+  byte = E - 2 + 127;
+  if (byte < 0) byte = 0;
+  if (byte > 254) byte = 254;
+  k2 = (2.5f - 2.0f * (float)(byte - 127)) - 2.0f * m;
+  for (k = 0; k < BLOCK; k++) {
+    a = fmaf(s[k], 2.0f * c, k2);
+    if (!(a > 0.0f)) a = 0.0f;
+    if (a > 7.5f) a = 7.5f;
+    codes[k] = (int)a;
   }
   return byte;
 }
@@ -668,7 +705,7 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
   int64_t h, i, j, c, kk, nbk;
   float c2;
   double *vhat = 0, *acc = 0;
-  float *t = 0;
+  float *t = 0, *sr = 0;
   if (!get_fmt(v_fmt, &fv) || v_fmt == MXREF_AXS6 || (v_fmt & ~0xFF)) return -1;
   get_fmt(MXREF_FP4_E2M1, &fp);
   if (block != BLOCK || heads < 0 || lq < 0 || d <= 0 || lk <= 0 ||
@@ -681,8 +718,9 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
   vhat = (double *)malloc(sizeof(double) * (size_t)(d * lk));
   acc = (double *)malloc(sizeof(double) * (size_t)d);
   t = (float *)malloc(sizeof(float) * (size_t)lk);
-  if (!vhat || !acc || !t) {
-    free(vhat); free(acc); free(t);
+  sr = (float *)malloc(sizeof(float) * (size_t)lk);
+  if (!vhat || !acc || !t || !sr) {
+    free(vhat); free(acc); free(t); free(sr);
     return -1;
   }
   for (h = 0; h < heads; h++) {
@@ -709,7 +747,8 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
         const uint16_t *kr = k + (h * lk + kk) * d;
         double s = 0.0;
         for (c = 0; c < d; c++) s += bf16_value(qi[c]) * bf16_value(kr[c]);
-        t[kk] = (float)s * c2;
+        sr[kk] = (float)s;
+        t[kk] = sr[kk] * c2;
         if ((float)s * scale > row_top) row_top = (float)s * scale;
       }
       for (c = 0; c < d; c++) acc[c] = 0.0;
@@ -733,7 +772,7 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
             for (e = 0; e < BLOCK; e++) pv[e] = (double)mxref_exp2(dv[e]);
             byte = quantize_values(&fp, MXREF_FP4_E2M1, pv, codes);
           } else {
-            byte = mxref_efq_block_log2(dv, codes);
+            byte = mxref_efq_attention_block(sr + kk, c2, m, codes);
           }
           for (e = 0; e < BLOCK; e++)
             phat[e] = byte == 0xFF ? NAN
@@ -755,6 +794,7 @@ static int attention_fwd(int rule, int v_fmt, int block, const uint16_t *q,
   free(vhat);
   free(acc);
   free(t);
+  free(sr);
   return 0;
 }
 
@@ -770,7 +810,8 @@ int mxref_attention_fwd(int v_fmt, int block, const uint16_t *q,
 }
 
 /* the same forward with EFQ's exp-free probability blocks (a reading,
- * parity unpinned by the pages; see mxref_efq_block) */
+ * parity unpinned by the pages; see mxref_efq_block and, for the form used
+ * here, mxref_efq_attention_block) */
 int mxref_attention_fwd_efq(int v_fmt, int block, const uint16_t *q,
                             const uint16_t *k, const uint8_t *v_codes,
                             const uint8_t *v_scales, int64_t heads,

@@ -81,6 +81,9 @@ int mxref_efq_block(const float *dv, int *codes);
 int mxref_efq_quantize_block(const float *dv, uint8_t *packed);
 /* the same on shifted scores already in powers of two (u = d log2 e) */
 int mxref_efq_block_log2(const float *u, int *codes);
+/* the attention forward's form: raw scores s, c = fp32(scale log2 e), the
+ * running maximum m of fp32(s c); the affine map as one fused multiply-add */
+int mxref_efq_attention_block(const float *s, float c, float m, int *codes);
 int mxref_efq_quantize_block_log2(const float *u, uint8_t *packed);
 int mxref_attention_fwd_efq(int v_fmt, int block, const uint16_t *q,
                             const uint16_t *k, const uint8_t *v_codes,

@@ -5,8 +5,9 @@ taken from the largest value in the block, then one affine map from shifted scor
 nonnegative E2M1 codes, no exp) but prints no constants, so the oracle
 implements a stated reading: u = fp32(d log2 e), byte = the MX rule on 2^U
 (U = max u), w = u - (byte - 127), code = trunc(clamp(2w + 2.5, 0, 7.5)); the
-attention forward, whose scores are already in powers of two, hands in
-u = t - m directly (efq_block_log2).
+attention forward, whose scores are already in powers of two, applies the
+rule to u = t - m and evaluates the affine map from the raw score in one
+fused multiply-add (efq_attention_block).
 PARITY UNPINNED by the pages: these tests pin the reading's own properties
 (exact powers of two land on the even codes, monotonicity, the block
 maximum's code, the log-domain rounding bound, agreement with
@@ -165,14 +166,54 @@ def test_attention_blocks_follow_the_block_rule():
     o, m, l, pc, ps = oracle.attention_fwd(oracle.FP8_E4M3, q, k, vc, vs, scale, efq=True)
     s = np.einsum("hqd,hkd->hqk", workloads.bf16_bits_to_f32(q).astype(np.float64),
                   workloads.bf16_bits_to_f32(k).astype(np.float64)).astype(np.float32)
-    # the forward's scores in powers of two: t = fp32(s * fp32(scale * log2 e))
-    t = (s * np.float32(scale * LOG2E)).astype(np.float32)
+    # the forward's scores in powers of two: t = fp32(s * c), c = fp32(scale * log2 e);
+    # its blocks are the attention form of the rule (the affine map as one
+    # fused multiply-add from the raw score), which must agree with the
+    # stand-alone rule on u = t - m: the same scale bytes, and codes that
+    # differ only where the two roundings straddle a code boundary
+    c = np.float32(scale * LOG2E)
+    t = (s * c).astype(np.float32)
+    nib = lambda x: np.stack([x & 15, x >> 4], -1).reshape(-1).astype(np.int64)
+    moved, total = 0, 0
     for h in range(heads):
         for i in range(lq):
             run_max = np.float32(-np.inf)
             for j in range(0, lk, 64):
                 run_max = max(run_max, t[h, i, j:j + 64].max())
                 for b in range(j, min(j + 64, lk), 32):
-                    byte, packed = oracle.efq_quantize_block_log2((t[h, i, b:b + 32] - run_max)
-                                                                  .astype(np.float32))
-                    assert ps[h, i, b // 32] == byte and pc[h, i, b // 32].tobytes() == packed.tobytes()
+                    byte, codes = oracle.efq_attention_block(s[h, i, b:b + 32], c, run_max)
+                    assert ps[h, i, b // 32] == byte
+                    assert np.array_equal(nib(pc[h, i, b // 32]), codes)
+                    byte2, codes2 = oracle.efq_block_log2((t[h, i, b:b + 32] - run_max)
+                                                          .astype(np.float32))
+                    assert byte2 == byte and np.abs(codes - codes2).max() <= 1
+                    moved += int((codes != codes2).sum())
+                    total += 32
+    assert moved / total < 1e-3
+
+
+def test_attention_form_special_blocks():
+    c = np.float32(0.125 * LOG2E)
+    zero = np.zeros(32, np.float32)
+    # the block holding the running maximum: u = 0 there, code 6 (value 4 X = 1)
+    s = -np.abs(np.random.default_rng(7).standard_normal(32)).astype(np.float32)
+    s[5] = 0.0
+    byte, codes = oracle.efq_attention_block(s, c, np.float32(0.0))
+    assert byte == 125 and codes[5] == 6 and codes.max() == 6
+    # a NaN score poisons its block
+    s2 = zero.copy()
+    s2[3] = np.nan
+    assert oracle.efq_attention_block(s2, c, 0.0)[0] == 0xFF
+    # -inf scores under a finite maximum: byte 0 and no codes
+    byte, codes = oracle.efq_attention_block(np.full(32, -np.inf, np.float32), c, 1.0)
+    assert byte == 0 and not codes.any()
+    # an infinite maximum: finite scores give u = -inf (byte 0, no codes);
+    # an infinite score gives inf - inf and poisons the block
+    byte, codes = oracle.efq_attention_block(zero, c, np.inf)
+    assert byte == 0 and not codes.any()
+    s3 = zero.copy()
+    s3[0] = np.inf
+    assert oracle.efq_attention_block(s3, c, np.inf)[0] == 0xFF
+    # scores far below the maximum: byte 0 and no codes (no overflow on the way)
+    byte, codes = oracle.efq_attention_block(np.full(32, -1e30, np.float32), c, 5.0)
+    assert byte == 0 and not codes.any()
