@@ -112,9 +112,9 @@ __device__ __forceinline__ uint32_t canon_nan16x2(uint32_t u) {
 constexpr int kTile = 64;  // blocks per wave tile (one per lane)
 
 template <int NCH>
-__device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void* y, int64_t b0,
-                                                   int64_t nb, int lane,
-                                                   const uint32_t (&d)[4 * NCH]) {
+__device__ __forceinline__ void store_tile_via_lds_full(uint4* __restrict__ lds, void* y,
+                                                        int64_t b0, int64_t nb, int lane,
+                                                        const uint32_t (&d)[4 * NCH]) {
   constexpr int P = NCH + 1;
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
@@ -133,6 +133,57 @@ __device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The same for 128-byte (fp32) blocks in two rounds of 32 lanes, through a
+// tile half the size (32 rows of NCH+1 chunks), so that a workgroup needs
+// 18 KB of LDS instead of 37 KB and twice as many fit on a CU: lanes 0..31
+// park their blocks and the wave stores them (4 KB, four 1 KB
+// instructions), then lanes 32..63 do the same.
+template <int NCH>
+__device__ __forceinline__ void store_tile_via_lds_halves(uint4* __restrict__ lds, void* y,
+                                                          int64_t b0, int64_t nb, int lane,
+                                                          const uint32_t (&d)[4 * NCH]) {
+  constexpr int P = NCH + 1;
+  constexpr int HALF = kTile / 2;  // blocks per round
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((lane >> 5) == half) {
+      const int row = lane & (HALF - 1);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        lds[row * P + i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t hb0 = b0 + half * HALF;
+    const int64_t left = nb - hb0;
+    const int64_t valid = (left < 0 ? 0 : (left < HALF ? left : HALF)) * NCH;
+    uint4* dst = reinterpret_cast<uint4*>(y) + hb0 * NCH;
+#pragma unroll
+    for (int i = 0; i < HALF * NCH / 64; ++i) {
+      const int c = i * 64 + lane;
+      if (c < valid) dst[c] = lds[(c / NCH) * P + (c % NCH)];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// LDS slots per wave for a tile of NCH-chunk blocks, and the store that
+// uses them: fp32 blocks (NCH = 8) go out in two rounds through half a
+// tile (measured: the fp32 E2M1 dequantizer of the attention probabilities
+// 454 -> 438 us), bf16 blocks in one.
+constexpr int tile_slots(int nch) { return (nch == 8 ? kTile / 2 : kTile) * (nch + 1); }
+
+template <int NCH>
+__device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void* y, int64_t b0,
+                                                   int64_t nb, int lane,
+                                                   const uint32_t (&d)[4 * NCH]) {
+  if constexpr (NCH == 8) store_tile_via_lds_halves<NCH>(lds, y, b0, nb, lane, d);
+  else store_tile_via_lds_full<NCH>(lds, y, b0, nb, lane, d);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,7 +286,7 @@ __global__ __launch_bounds__(256) void dequantize_mx(const void* __restrict__ co
                                                      int64_t nb, void* __restrict__ y) {
   constexpr int W = Fmt<F>::W;
   constexpr int NCH = BF16 ? 4 : 8;  // 16-byte output chunks per block
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
@@ -270,7 +321,7 @@ template <int F, bool BF16>
 __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t nb, void* y) {
   constexpr int W = Fmt<F>::W;
   constexpr int NCH = BF16 ? 4 : 8;
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
@@ -377,7 +428,7 @@ __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x,
 template <bool BF16>
 __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t nb, void* y) {
   constexpr int NCH = BF16 ? 4 : 8;
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
@@ -434,7 +485,7 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
                                                        const uint8_t* __restrict__ aux, int64_t nb,
                                                        void* __restrict__ y) {
   constexpr int NCH = BF16 ? 4 : 8;
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
@@ -575,7 +626,7 @@ template <int W, bool BF16, bool M0>
 __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t nb, void* y,
                                                           ExmyParams p) {
   constexpr int NCH = BF16 ? 4 : 8;
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
@@ -611,7 +662,7 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
                                                        int64_t nb, void* __restrict__ y,
                                                        ExmyParams p) {
   constexpr int NCH = BF16 ? 4 : 8;
-  __shared__ uint4 lds[4][kTile * (NCH + 1)];
+  __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
