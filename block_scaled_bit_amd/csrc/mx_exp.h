@@ -1,5 +1,5 @@
-// mx_exp.h -- the fixed fp32 exp of the exp-then-quantize probabilities
-// (device code only).
+// mx_exp.h -- the fixed fp32 exp of the stand-alone exp-then-quantize
+// probabilities (device code only).
 //
 // Cody-Waite reduction (Cody and Waite, "Software Manual for the Elementary
 // Functions", 1980) with ln2 split into a 16-bit head and a tail, a degree-7
@@ -16,17 +16,15 @@ namespace mxk {
 
 // exp(d) for d <= 0 (shifted scores) and d = -inf (-> 0).  The reduction
 // runs on max(d, -104): from there the product below already rounds to +0,
-// which is the exact result for every d < -104 too.  kNaN: a NaN d gives NaN
-// (the clamp is then a comparison, one more instruction); otherwise the
-// caller guarantees d is not NaN.
-template <bool kNaN = false>
+// which is the exact result for every d < -104 too.  The caller guarantees
+// d is not NaN.
 __device__ __forceinline__ float exp_ref_nonpos(float d) {
   const float kLog2e = 0x1.715476p+0f;
   const float kLn2Hi = 0x1.62e400p-1f;
   const float kLn2Lo = 0x1.7f7d1cp-20f;
   const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
               k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
-  const float dc = kNaN ? (d < -104.0f ? -104.0f : d) : __builtin_fmaxf(d, -104.0f);
+  const float dc = __builtin_fmaxf(d, -104.0f);
   const float nf = __builtin_rintf(dc * kLog2e);
   float r = __builtin_fmaf(-nf, kLn2Hi, dc);
   r = __builtin_fmaf(-nf, kLn2Lo, r);
@@ -40,35 +38,6 @@ __device__ __forceinline__ float exp_ref_nonpos(float d) {
   p = __builtin_fmaf(p, r, 1.0f);
   // p * 2^n with one rounding (n in [-150, 0]; subnormal results rounded to
   // nearest even), the same value as exact power-of-two pre-scaling
-  return __builtin_ldexpf(p, (int)nf);
-}
-
-// The same sequence without the clamp, for callers that check the results.
-// For d >= -104 it is exp_ref_nonpos(d).  For -2^20 <= d < -104 it is 0 or
-// 2^-149 where exp_ref_nonpos gives 0: n <= -150, the reduced argument stays
-// within [-0.5, 0.5], so p * 2^n is at most 0.83 * 2^-149.  For d < -2^20 or
-// d = -inf it is +0, -0, +-inf or NaN (a huge n or a garbage reduction).  So
-// every result is either one that encodes like exp_ref_nonpos's (0 and
-// 2^-149 both round to the zero code under any block scale, and both give a
-// block of nothing else the scale byte 0), or has a bit pattern of at least
-// 0x7F800000, which the caller detects and then recomputes with the clamp.
-__device__ __forceinline__ float exp_ref_nonpos_unclamped(float d) {
-  const float kLog2e = 0x1.715476p+0f;
-  const float kLn2Hi = 0x1.62e400p-1f;
-  const float kLn2Lo = 0x1.7f7d1cp-20f;
-  const float k2 = 0x1.000000p-1f, k3 = 0x1.555556p-3f, k4 = 0x1.555556p-5f,
-              k5 = 0x1.111112p-7f, k6 = 0x1.6c16c2p-10f, k7 = 0x1.a01a02p-13f;
-  const float nf = __builtin_rintf(d * kLog2e);
-  float r = __builtin_fmaf(-nf, kLn2Hi, d);
-  r = __builtin_fmaf(-nf, kLn2Lo, r);
-  float p = k7;
-  p = __builtin_fmaf(p, r, k6);
-  p = __builtin_fmaf(p, r, k5);
-  p = __builtin_fmaf(p, r, k4);
-  p = __builtin_fmaf(p, r, k3);
-  p = __builtin_fmaf(p, r, k2);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
   return __builtin_ldexpf(p, (int)nf);
 }
 
