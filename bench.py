@@ -583,13 +583,13 @@ def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
     flops = 4.0 * heads * lq * lk * d
     scores = heads * lq * lk
     # fp32 VALU operations the method fixes per score -- exp-then-quantize:
-    # the scaling by scale * log2 e, the shift, the 2^u's 10 (rint, the
-    # reduction, 6 fused multiply-adds, the conversion of n, the scaling by
-    # 2^n) and the block maximum = 13; EFQ: the affine map from the raw
+    # the scaling by scale * log2 e, the shift, the 2^u's 9 (rint, the
+    # reduction, 5 fused multiply-adds, the conversion of n, the scaling by
+    # 2^n) and the block maximum = 12; EFQ: the affine map from the raw
     # score (one fused multiply-add, the clamp, the conversion) and the
     # block maximum = 4.  The chip issues 256 CUs x 4 SIMDs x 16 lanes x
     # 2.4 GHz of them per second.
-    for name, fn, ops_per in (("attention_fwd_e2m1_p_mxfp8_v", mx.mx_attention_fwd, 13.0),
+    for name, fn, ops_per in (("attention_fwd_e2m1_p_mxfp8_v", mx.mx_attention_fwd, 12.0),
                               ("attention_fwd_efq_e2m1_p_mxfp8_v", mx.mx_attention_fwd_efq, 4.0)):
         def step(i, fn=fn):
             st = fn(mx.MX_FP8_E4M3, 32, q, kk, vc, vs, heads, lq, lk, d, scale, mx.MX_BF16, o,

@@ -197,10 +197,10 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
  *   keys are taken 64 at a time: m_new = max(m, max t over the tile) (NaN
  *   scores are skipped by the maximum); if m_new > m the running sums are
  *   multiplied by 2^(m - m_new); p = 2^(t - m_new) with a fixed fp32 2^u
- *   (n = rint(u); the degree-6 polynomial interpolating 2^f at the seven
- *   Chebyshev points of [-1/2, 1/2], coefficients rounded to fp32, by
- *   Horner's rule with fused multiply-adds at f = u - n; scaling by 2^n
- *   with one rounding: within about one ulp of 2^u, exact at integers);
+ *   (n = rint(u); at f = u - n a degree-5 polynomial with constant term 1
+ *   and near-minimax fp32 coefficients, by Horner's rule with fused
+ *   multiply-adds; scaling by 2^n with one rounding: within 2.1 ulp of
+ *   2^u, exact at integers);
  *   p is quantized per 32 keys to E2M1 by the rules
  *   above (a NaN p gives a 0xFF block, which makes the row's output NaN);
  *   the numerator adds P * V, the denominator adds P * 1, both from the

@@ -448,17 +448,17 @@ float mxref_exp(float d) {
  * evaluates exp(t - m) as 2^((t - m) log2 e) with log2 e joined to the
  * score scale):
  *   n = rint(u),  f = u - n (exact, |f| <= 1/2),
- *   p = c0 + c1 f + ... + c6 f^6 by Horner's rule with fused multiply-adds,
+ *   p = 1 + c1 f + ... + c5 f^5 by Horner's rule with fused multiply-adds,
  *   2^u = p * 2^n with one rounding (exact multiplications by powers of two
  *   as in mxref_exp).
- * c0..c6 are the coefficients of the degree-6 polynomial interpolating 2^f
- * at the seven Chebyshev points cos((2k+1) pi / 14) / 2 of [-1/2, 1/2],
- * each rounded to fp32; one of the points is f = 0, so c0 = 1 exactly and
- * 2^u is exact for every integer u in [-149, 0]. */
+ * c1..c5 minimize the largest relative error of 1 + f (c1 + ... + c5 f^4)
+ * against 2^f over [-1/2, 1/2] (a linear program on a dense grid; the
+ * constant term is held at 1, so 2^u is exact for every integer u in
+ * [-149, 0]), each then moved by a few fp32 ulps to the values whose fp32
+ * evaluation errs least.  The result is within 2.1 ulp of 2^u. */
 float mxref_exp2(float u) {
-  const float C0 = 0x1.000000p+0f, C1 = 0x1.62e430p-1f, C2 = 0x1.ebfbe0p-3f,
-              C3 = 0x1.c6aeccp-5f, C4 = 0x1.3b2a1cp-7f, C5 = 0x1.5f48c0p-10f,
-              C6 = 0x1.444000p-13f;
+  const float C1 = 0x1.62e42ap-1f, C2 = 0x1.ebf994p-3f, C3 = 0x1.c6b5acp-5f,
+              C4 = 0x1.3cf68ap-7f, C5 = 0x1.5c54b4p-10f;
   float nf, f, p;
   int n;
   if (isnan(u)) return u;
@@ -466,13 +466,12 @@ float mxref_exp2(float u) {
   if (u < -151.0f) return 0.0f;
   nf = rintf(u);
   f = u - nf;
-  p = C6;
-  p = fmaf(p, f, C5);
+  p = C5;
   p = fmaf(p, f, C4);
   p = fmaf(p, f, C3);
   p = fmaf(p, f, C2);
   p = fmaf(p, f, C1);
-  p = fmaf(p, f, C0);
+  p = fmaf(p, f, 1.0f);
   n = (int)nf;
   if (n < -100) { p = p * 0x1p-50f; n += 50; }
   if (n > 100) { p = p * 0x1p+50f; n -= 50; }

@@ -532,7 +532,7 @@ def test_exp_ref_subnormal_range_and_monotone():
 # (g2) the attention forward's base-2 exponential
 # ----------------------------------------------------------------------------
 def _exp2_literals():
-    """The coefficients C0..C6 as written in mxref_exp2's source."""
+    """The coefficients C1..C5 as written in mxref_exp2's source."""
     src = open(os.path.join(os.path.dirname(oracle.__file__), "mxref.c")).read()
     body = src[src.index("float mxref_exp2(float u)"):]
     body = body[:body.index("float nf")]
@@ -540,16 +540,29 @@ def _exp2_literals():
             for j, v in re.findall(r"C(\d) = (0x[0-9a-f.]+p[+-]\d+)f", body)}
 
 
-def test_exp2_coefficients_are_the_chebyshev_interpolant():
-    # the stated definition, computed here in float64: the degree-6
-    # polynomial through 2^x at the Chebyshev points cos((2k+1) pi/14)/2
-    n = 7
-    x = np.cos((2 * np.arange(n) + 1) * np.pi / (2 * n)) / 2
-    c = np.linalg.solve(np.vander(x, n, increasing=True), np.exp2(x))
+def test_exp2_coefficients_are_a_constrained_minimax_polynomial():
+    # the stated construction, computed here: the smallest possible largest
+    # relative error of 1 + f (c1 + c2 f + ... + c5 f^4) against 2^f on
+    # [-1/2, 1/2] (a linear program on a grid); in exact arithmetic the
+    # literals come within 1.5x of it (they were moved a few fp32 ulps from
+    # the optimum towards the values whose fp32 evaluation errs least)
+    from scipy.optimize import linprog
+    f = np.linspace(-0.5, 0.5, 4001)
+    ex = np.exp2(f)
+    V = np.stack([f ** (j + 1) for j in range(5)], 1)
+    A = np.vstack([np.hstack([V, -ex[:, None]]), np.hstack([-V, -ex[:, None]])])
+    b = np.r_[ex - 1, 1 - ex]
+    res = linprog(np.r_[np.zeros(5), 1.0], A_ub=A, b_ub=b, bounds=[(None, None)] * 6,
+                  method="highs")
+    assert res.success and res.x[-1] < 1e-7  # under one fp32 ulp of 1
     lit = _exp2_literals()
-    assert sorted(lit) == list(range(n))
-    assert [np.float32(c[j]) for j in range(n)] == [np.float32(lit[j]) for j in range(n)]
-    assert lit[0] == 1.0 and abs(c[0] - 1.0) < 1e-15  # the node x = 0
+    assert sorted(lit) == [1, 2, 3, 4, 5]
+    g = np.linspace(-0.5, 0.5, 200001)
+    p = np.zeros_like(g)
+    for j in (5, 4, 3, 2, 1):
+        p = (p + lit[j]) * g
+    err = np.max(np.abs((1.0 + p) / np.exp2(g) - 1.0))
+    assert err <= 1.5 * res.x[-1], (err, res.x[-1])
 
 
 def _ulps(p, ref):
@@ -560,16 +573,17 @@ def _ulps(p, ref):
     return np.abs(p - ref) / ulp
 
 
-def test_exp2_ref_within_one_ulp():
-    # (over every fp32 f in [-1/2, 1/2], the whole reduced range, the
-    # largest error is 0.992 ulp; the scaling by 2^n keeps the count)
+def test_exp2_ref_within_its_bound():
+    # within 2.1 ulp (over every fp32 f in [-1/2, 1/2], the whole reduced
+    # range, the largest error is 2.093 ulp; the scaling by 2^n keeps the
+    # count)
     rng = np.random.default_rng(21)
     u = np.concatenate([np.linspace(-0.5, 0.5, 400001), rng.uniform(-0.5, 0.5, 300000),
                         rng.uniform(-151.0, 0.0, 300000), -rng.exponential(4.0, 100000)])
     u = u.astype(np.float32)
     err = _ulps(oracle.exp2_ref(u).astype(np.float64), np.exp2(u.astype(np.float64)))
-    assert err.max() <= 1.0, err.max()
-    assert np.mean(err <= 0.5) > 0.9
+    assert err.max() <= 2.1, err.max()
+    assert np.mean(err <= 1.0) > 0.7
 
 
 def test_exp2_ref_special_values():
@@ -588,15 +602,15 @@ def test_exp2_ref_special_values():
 def test_exp2_ref_agrees_with_exp_ref_in_base_e():
     # exp_ref(d) and exp2_ref(fp32(d log2 e)) evaluate the same function;
     # they differ by the roundings of log2 e and of d log2 e (together
-    # <= |u| 2^-23 in the exponent, a relative ln2 |u| 2^-23) plus an ulp
-    # or two
+    # <= |u| 2^-23 in the exponent, a relative ln2 |u| 2^-23) plus the two
+    # evaluations' own errors (2 and 2.1 ulp)
     rng = np.random.default_rng(22)
     d = -np.abs(rng.standard_normal(200000) * 8).astype(np.float32)
     u = (d * np.float32(1.4426950408889634)).astype(np.float32)
     a = oracle.exp2_ref(u).astype(np.float64)
     b = _exp_many(d).astype(np.float64)
     rel = np.abs(a - b) / b
-    assert np.all(rel <= np.log(2) * np.abs(u) * 2.0 ** -23 + 4 * 2.0 ** -24)
+    assert np.all(rel <= np.log(2) * np.abs(u) * 2.0 ** -23 + 9 * 2.0 ** -24)
 
 
 def test_softmax_quantize_structure():
