@@ -16,14 +16,15 @@
 //                            (query, 32-key block) pair with no exchange
 //   t    = S * c with c = scale * log2(e) (scores in powers of two); tile
 //          max; rescale O and l when the maximum grows
-//   p    = 2^(t - m) (exp2_ref); block scale byte; 16 E2M1 codes per lane, which
-//          are exactly the lane's B operand of the block-scaled MFMA
+//   p    = 2^(t - m) (exp2_ref); block scale byte; 16 E2M1 codes per lane,
+//          which are exactly the lane's B operand of the block-scaled MFMA
+//          (EFQ: codes from one fused multiply-add per raw score instead)
 //   O^T += V^T * P^T         4 block-scaled 32x32x64 MFMAs (V in E4M3,
 //                            E2M3, E3M2 or E2M1, P in E2M1)
 //   l   += 1 * P^T           one more block-scaled MFMA with an all-ones A
 // so the probabilities never leave registers and the PV product and the
-// normalizing sum consume the same E2M1 operand.  K and V^T tiles are staged in
-// LDS once per workgroup and shared by its 4 waves.
+// normalizing sum consume the same E2M1 operand.  K and V^T tiles are
+// staged in LDS once per workgroup and shared by its 4 waves.
 //
 // Operand layouts (checked on the hardware by the library's probe tests):
 //   bf16 32x32x16: lane l holds A[l%32][8(l/32) + e] and B[8(l/32) + e][l%32]
