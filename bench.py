@@ -98,6 +98,66 @@ def time_launches(fn, nsets, steps, warmup, min_warm_s=0.0):
     return t0.elapsed_time(t1) / steps
 
 
+def _smi_clock_doc(text):
+    """The "clock" object of amd-smi's JSON list, found among whatever else
+    the tool prints (warnings before or after it)."""
+    dec = json.JSONDecoder()
+    start = text.find("[")
+    while start >= 0:
+        try:
+            doc, _ = dec.raw_decode(text[start:])
+            if isinstance(doc, list) and doc and isinstance(doc[0], dict) and "clock" in doc[0]:
+                return doc[0]["clock"]
+        except ValueError:
+            pass
+        start = text.find("[", start + 1)
+    raise ValueError("no clock list in the output")
+
+
+def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
+    """The GPU's clocks as amd-smi reports them while `step` (the headline
+    kernel) runs back to back: per sample the mean, lowest and highest of
+    the eight XCDs' graphics clocks, the memory clock and the rated
+    maximum, in MHz.  None when the tool is missing; a sample that fails
+    records the error.  Reported beside the timing, never used by it."""
+    import shutil
+    import subprocess
+    import threading
+    import time
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    readings = []
+
+    def sample():
+        for _ in range(samples):
+            time.sleep(seconds / (samples + 1))
+            try:
+                r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                c = _smi_clock_doc(r.stdout)
+                gfx = [v["clk"]["value"] for k, v in c.items() if k.startswith("gfx_")]
+                readings.append({"gfx_mean_MHz": round(sum(gfx) / len(gfx)),
+                                 "gfx_min_MHz": min(gfx), "gfx_max_MHz": max(gfx),
+                                 "mem_MHz": c.get("mem_0", {}).get("clk", {}).get("value"),
+                                 "gfx_rated_max_MHz": c["gfx_0"]["max_clk"]["value"]})
+            except Exception as e:  # a reading, not a measurement: never fatal
+                readings.append({"error": type(e).__name__})
+
+    th = threading.Thread(target=sample)
+    th.start()
+    i = 0
+    while th.is_alive():
+        for _ in range(64):
+            step(i % nsets)
+            i += 1
+        torch.cuda.synchronize()
+    th.join()
+    return {"samples": readings, "tool": "amd-smi metric -c --json",
+            "note": "sampled while the headline kernel runs back to back after the timed region"}
+
+
 def bf16_dev(bits_np, copies):
     import numpy as np
     import torch
@@ -123,6 +183,7 @@ def headline(mx, x_np, steps, warmup):
             raise mx.MxError(st, "mx_quantize")
 
     ms = time_launches(step, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
+    clocks = gpu_clocks_under_load(step, nsets)
 
     # the same HBM, same rotation: torch's device-to-device copy of the input
     # (reads and writes in_bytes each), a reference rate, not a ceiling
@@ -151,7 +212,7 @@ def headline(mx, x_np, steps, warmup):
         # gets the quantizer's output back for the parity check
         step(0)
         torch.cuda.synchronize()
-    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, sched
+    return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, sched, clocks
 
 
 def rows_floor_probe():
@@ -712,8 +773,8 @@ def main():
         return
 
     x = workloads.linear_weight()
-    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs, sched = headline(mx, x, args.steps,
-                                                                        args.warmup)
+    ms, in_b, alg_b, nsets, codes0, scales0, copy_gbs, sched, clocks = headline(
+        mx, x, args.steps, args.warmup)
     achieved = alg_b / ms / 1e6
     digest = source_digest()
     out = {
@@ -742,6 +803,7 @@ def main():
                                "note": "torch's device-to-device copy of the bf16 input (read + "
                                        "write bytes / time), same buffers and rotation; a "
                                        "reference rate, not a ceiling"},
+        "gpu_clocks": clocks,
     }
     if sched:
         best = min(MIX_COPIES, key=lambda k: sched[k])
