@@ -183,6 +183,10 @@ def headline(mx, x_np, steps, warmup):
             raise mx.MxError(st, "mx_quantize")
 
     ms = time_launches(step, nsets, steps, warmup, min_warm_s=SECONDARY_WARM_S)
+    # the same launches again as 5 batches of steps/5, each between its own
+    # events: the spread of the per-launch time, and its median
+    per = max(1, steps // 5)
+    batches = sorted(time_launches(step, nsets, per, 0) for _ in range(5))
     clocks = gpu_clocks_under_load(step, nsets)
 
     # the same HBM, same rotation: torch's device-to-device copy of the input
@@ -212,6 +216,9 @@ def headline(mx, x_np, steps, warmup):
         # gets the quantizer's output back for the parity check
         step(0)
         torch.cuda.synchronize()
+    clocks = {"gpu_clocks": clocks, "batches": {
+        "count": 5, "launches_each": per, "median_us": round(batches[2] * 1e3, 3),
+        "min_us": round(batches[0] * 1e3, 3), "max_us": round(batches[-1] * 1e3, 3)}}
     return ms, in_bytes, in_bytes + out_bytes, nsets, codes[0], scales[0], copy_gbs, sched, clocks
 
 
@@ -803,7 +810,8 @@ def main():
                                "note": "torch's device-to-device copy of the bf16 input (read + "
                                        "write bytes / time), same buffers and rotation; a "
                                        "reference rate, not a ceiling"},
-        "gpu_clocks": clocks,
+        "batches": clocks["batches"],
+        "gpu_clocks": clocks["gpu_clocks"],
     }
     if sched:
         best = min(MIX_COPIES, key=lambda k: sched[k])
