@@ -379,10 +379,13 @@ def attention_fwd(q: torch.Tensor, k: torch.Tensor, v_codes: torch.Tensor,
                   v_scales: torch.Tensor, v_fmt="mxfp8", scale=None, out_dtype=torch.bfloat16,
                   stats: bool = False, probs: bool = False, efq: bool = False):
     """Attention forward with E2M1 probabilities.  q [heads, lq, 128] and k
-    [heads, lk, 128] bf16; V given as ``quantize_v`` returns it.  Returns o
-    [heads, lq, 128]; with stats=True also (row_max, row_sum); with
-    probs=True also the E2M1 probability blocks (p_codes, p_scales).
-    efq=True: the exp-free EFQ probability rule (mx_attention_fwd_efq)."""
+    [heads, lk, 128] bf16; V given as ``quantize_v`` returns it; scale
+    defaults to 1/sqrt(128) and must be positive.  The probabilities are
+    2^(t - m) of the scores in powers of two, t = s * scale * log2(e).
+    Returns o [heads, lq, 128]; with stats=True also (row_max in natural
+    units, row_sum); with probs=True also the E2M1 probability blocks
+    (p_codes, p_scales).  efq=True: the exp-free EFQ probability rule
+    (mx_attention_fwd_efq)."""
     f = _fmt(v_fmt)
     if f not in _V_FORMATS:
         raise MxError(4, f"V format {v_fmt}")
