@@ -71,36 +71,11 @@ __device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_bits) {
 }
 
 // ---------------------------------------------------------------------------
-// AXS-6 rounding in software (there is no hardware AXS-6 format): the scaled
-// magnitude a = |v| * 2^(127 - byte) is exact (fp32 ldexp of a bf16/fp32
-// value; only values far below the grid's half step can lose bits, and they
-// round to zero either way), clamped to 31/16, and m = rint(16 a) rounds to
-// nearest even on the 1/16 grid.
+// AXS-6 in software (there is no hardware AXS-6 format).  The kernels round
+// m = rint(|v| 2^(131 - byte)) (16 |v| / X exactly: a value small enough to
+// lose bits in that power-of-two scaling rounds to 0 either way) to nearest
+// even and clamp it to 31; decoding is the exact m 2^(byte - 131).
 // ---------------------------------------------------------------------------
-struct Rounded {
-  uint32_t mag;  // magnitude code m
-  float val;     // m / 16, the rounded magnitude in units of the block scale
-};
-
-template <int F>
-__device__ __forceinline__ Rounded round_scaled(float a) {
-  static_assert(Fmt<F>::FIXED, "software rounding is used for AXS-6 only");
-  Rounded out;
-  float m = __builtin_rintf(a * 16.0f);  // a * 16 is exact; RNE
-  m = fminf(m, 31.0f);
-  out.mag = (uint32_t)m;
-  out.val = m * 0.0625f;
-  return out;
-}
-
-// Scaled, clamped magnitude of one input value (fp32 bit pattern).
-template <int F>
-__device__ __forceinline__ float scaled_abs(uint32_t vbits, int neg_exp) {
-  float av = __uint_as_float(vbits & 0x7FFFFFFFu);
-  float a = __builtin_ldexpf(av, neg_exp);
-  return fminf(a, Fmt<F>::MAXF);
-}
-
 // Unscaled AXS-6 value m/16 times 2^scale_exp (exact in fp32).
 template <int F>
 __device__ __forceinline__ float decode_mag(uint32_t mag, int scale_exp) {
