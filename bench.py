@@ -128,13 +128,19 @@ def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
+    cmd = [exe]
+    with open(exe, "rb") as f:
+        if b"python" in f.readline():
+            # a Python script: start it with this interpreter, so that no
+            # `#!/usr/bin/env` launcher replaces itself with python
+            cmd = [sys.executable, exe]
     readings = []
 
     def sample():
         for _ in range(samples):
             time.sleep(seconds / (samples + 1))
             try:
-                r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True,
+                r = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True,
                                    text=True, timeout=10)
                 c = _smi_clock_doc(r.stdout)
                 gfx = [v["clk"]["value"] for k, v in c.items() if k.startswith("gfx_")]
