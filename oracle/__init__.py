@@ -27,12 +27,11 @@ NAMES = {"mxfp6_e2m3": FP6_E2M3, "mxfp6_e3m2": FP6_E3M2, "mxfp4": FP4_E2M1,
 
 def exmy(e: int, m: int) -> int:
     """Identifier of the generic eXmY format with e exponent and m mantissa
-    bits (width 1 + e + m, 3..9 bits, e <= 7)."""
+    bits (width 1 + e + m, 3..9 bits, so e <= 8)."""
     return 0x100 | (e << 4) | m
 
 
-EXMY_FORMATS = [exmy(e, w - 1 - e) for w in range(3, 10) for e in range(0, min(w - 1, 7) + 1)
-                if w - 1 - e >= 0]
+EXMY_FORMATS = [exmy(e, w - 1 - e) for w in range(3, 10) for e in range(0, w)]
 
 
 class _Table(dict):

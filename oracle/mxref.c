@@ -73,13 +73,15 @@ static const fmt_t FORMATS[5] = {
 /* Generic eXmY formats ([EXMY] abstract: every split of a bit width   */
 /* into exponent and mantissa bits, e.g. e0m6 .. e6m0 for 7 bits).      */
 /* Identifier 0x100 | e << 4 | m; width w = 1 + e + m, 3 <= w <= 9,     */
-/* e <= 7.  Reading: sign-magnitude, IEEE-style fields with bias        */
+/* so e <= 8 (e8m0: zero and 2^-126 .. 2^128, whose largest magnitudes */
+/* and scaled values lie beyond fp32; this code works in doubles).      */
+/* Reading: sign-magnitude, IEEE-style fields with bias                 */
 /* 2^(e-1) - 1 and subnormals, every code finite (no inf/NaN codes, as  */
 /* in the OCP FP6/FP4 formats); e = 0 is a plain integer magnitude m.   */
 /* ------------------------------------------------------------------ */
 static int make_exmy(int e, int m, fmt_t *f) {
   int w = 1 + e + m;
-  if (e < 0 || m < 0 || e > 7 || w < 3 || w > 9) return 0;
+  if (e < 0 || m < 0 || e > 8 || w < 3 || w > 9) return 0;
   f->bits = w;
   f->ebits = e;
   f->mbits = m;

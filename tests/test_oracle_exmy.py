@@ -27,10 +27,10 @@ def test_every_split_of_3_to_9_bits():
     splits = {(f >> 4) & 15: [] for f in EXMY}
     widths = sorted({1 + ((f >> 4) & 15) + (f & 15) for f in EXMY})
     assert widths == list(range(3, 10))
-    for w in range(3, 9):  # every split of the w-1 non-sign bits
+    for w in range(3, 10):  # every split of the w-1 non-sign bits
         got = sorted(((f >> 4) & 15, f & 15) for f in EXMY if 1 + ((f >> 4) & 15) + (f & 15) == w)
         assert got == [(e, w - 1 - e) for e in range(w)], w
-    assert len(EXMY) == 41 and splits  # e8m0 is the one split left out (fp32 range)
+    assert len(EXMY) == 42 and splits
 
 
 @pytest.mark.parametrize("fmt", EXMY, ids=ids)
@@ -66,11 +66,59 @@ def test_grids_closed_forms():
     for m in range(1, 8):  # e1mY: the same uniform grid as e0m(Y+1), step 2^(1-Y)
         assert np.array_equal(brute.grid(oracle.exmy(1, m)),
                               np.arange(2 ** (m + 1)) * 2.0 ** (1 - m))
-    for e in range(2, 8):  # eXm0: zero and powers of two
+    for e in range(2, 9):  # eXm0: zero and powers of two (e8m0: 2^-126 .. 2^128)
         bias = 2 ** (e - 1) - 1
         want = np.concatenate([[0.0], 2.0 ** (np.arange(1, 2 ** e) - bias)])
         assert np.array_equal(brute.grid(oracle.exmy(e, 0)), want)
     assert oracle.BYTES_PER_BLOCK[oracle.exmy(3, 3)] == 28  # 32 x 7 bits, no padding
+    assert oracle.BYTES_PER_BLOCK[oracle.exmy(8, 0)] == 36  # 32 x 9 bits
+
+
+def test_e8m0_grid_is_torch_float8_e8m0fnu_between_its_ends():
+    # fields 1..254 are 2^(f - 127), as in the E8M0 scale type; eXmY's field
+    # 0 is zero (a subnormal with no mantissa bits) and 255 is finite, 2^128
+    g = brute.grid(oracle.exmy(8, 0))
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(g[1:255], lib[1:255])
+    assert g[0] == 0.0 and g[255] == 2.0 ** 128 and np.isnan(lib[255])
+
+
+def test_e8m0_beyond_the_fp32_range():
+    f = oracle.exmy(8, 0)
+    fmax = np.finfo(np.float32).max
+    # the block maximum sits in the top binade [2^128, 2^129) of the scaled
+    # values: byte = floor(log2 amax) - 128 + 127
+    x = np.zeros((1, 32), np.float32)
+    x[0, :5] = [fmax, 2.0 ** 127, 1.5 * 2.0 ** 126, 1.25 * 2.0 ** 126, 3.0 * 2.0 ** -127]
+    codes, scales, _ = oracle.quantize(f, x)
+    assert scales[0, 0] == 126  # X = 2^-1
+    c = brute.unpack(f, codes[0, 0].tobytes())
+    # fmax / X is just under 2^129: saturates to 2^128 (field 255); 2^127 / X
+    # is 2^128 itself; 1.5 2^127 is a tie between fields 254 and 255 and
+    # goes to the even field; 1.25 2^127 rounds down; 3 2^-126 is a tie
+    # between fields 2 and 3 (2^-125, 2^-124) and goes to field 2
+    assert list(c[:5]) == [255, 255, 254, 254, 2]
+    y = oracle.fake_quantize(f, x)
+    assert list(y[0, :5]) == [2.0 ** 127, 2.0 ** 127, 2.0 ** 126, 2.0 ** 126, 2.0 ** -126]
+    # a block whose maximum is below 2 takes the clamped byte 0, X = 2^-127
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [1.0, 2.0 ** -126, 1.5 * 2.0 ** -127, 2.0 ** -149]
+    codes, scales, _ = oracle.quantize(f, x)
+    assert scales[0, 0] == 0
+    assert list(brute.unpack(f, codes[0, 0].tobytes())[:4]) == [254, 128, 128, 105]
+
+
+def test_e8m0_dequantize_overflows_and_underflows_like_the_exact_product():
+    f = oracle.exmy(8, 0)
+    nb = 6
+    packed = b"".join(brute.pack(f, [c] + [0] * 31) for c in (255, 255, 1, 1, 2, 0x1FF))
+    codes = np.frombuffer(packed, np.uint8).reshape(nb, 36)
+    scales = np.array([127, 126, 104, 103, 103, 126], np.uint8)
+    y = oracle.dequantize(f, codes, scales, None, nb, 32, oracle.FP32).reshape(nb, 32)[:, 0]
+    # 2^128 overflows fp32; 2^127; 2^-149 is the smallest subnormal; 2^-150
+    # is a tie between 0 and 2^-149 and rounds to 0; 2^-125 2^-24 = 2^-149;
+    # -2^128 2^-1 = -2^127
+    assert list(y) == [np.inf, 2.0 ** 127, 2.0 ** -149, 0.0, 2.0 ** -149, -(2.0 ** 127)]
 
 
 def _anchored(E, values_bits):
@@ -109,19 +157,22 @@ def test_quantize_bf16_vs_brute_force(fmt):
 def test_ties_and_neighbours(fmt):
     # every midpoint between neighbouring grid values: ties go to the even
     # code (for m = 0 that is the even exponent field, not the larger value)
-    g = brute.finite_grid(fmt)
+    # the grid times X = 2^-sh, which keeps it inside fp32 (e8m0 reaches
+    # 2^128; its values times 1/2 are still exact there)
+    sh = max(0, brute.emax(fmt) - 127)
+    g = brute.finite_grid(fmt) * 2.0 ** -sh
     mids = ((g[:-1] + g[1:]) / 2.0).astype(np.float32)
     vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)),
                            np.nextafter(mids, np.float32(1e30)), g.astype(np.float32)])
     vals = np.concatenate([vals, -vals])
-    top = np.float32(2.0 ** brute.emax(fmt))
+    top = np.float32(2.0 ** (brute.emax(fmt) - sh))
     nblk = (len(vals) + 30) // 31
     blocks = np.empty((nblk, 32), np.float32)
     blocks[:, 0] = top
     blocks[:, 1:] = np.resize(vals, nblk * 31).reshape(nblk, 31)
     codes, scales, _ = oracle.quantize(fmt, blocks)
-    assert np.all(scales == 127)
-    want = brute.encode(fmt, blocks.reshape(-1).astype(np.float64), 127).reshape(-1, 32)
+    assert np.all(scales == 127 - sh)
+    want = brute.encode(fmt, blocks.reshape(-1).astype(np.float64), 127 - sh).reshape(-1, 32)
     got = np.array([brute.unpack(fmt, codes[i, 0].tobytes()) for i in range(nblk)])
     assert np.array_equal(got, want)
 
