@@ -30,7 +30,7 @@ BLOCK = 32
 
 
 def MX_EXMY(e: int, m: int) -> int:
-    """Generic eXmY format id (width 1 + e + m in 3..9, e <= 7), as mx.h."""
+    """Generic eXmY format id (width 1 + e + m in 3..9, so e <= 8), as mx.h."""
     return 0x100 | (e << 4) | m
 
 

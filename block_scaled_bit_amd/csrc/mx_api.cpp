@@ -19,7 +19,7 @@ int exmy_width(int f) { return 1 + exmy_e(f) + exmy_m(f); }
 
 bool fmt_ok(int f) {
   if (f >= MX_FP6_E2M3 && f <= MX_AXS6) return true;
-  return is_exmy(f) && exmy_e(f) <= 7 && exmy_width(f) >= 3 && exmy_width(f) <= 9;
+  return is_exmy(f) && exmy_width(f) >= 3 && exmy_width(f) <= 9;
 }
 
 int bytes_per_block(int f) { return is_exmy(f) ? 4 * exmy_width(f) : kBytesPerBlock[f]; }
@@ -34,7 +34,9 @@ mxk::ExmyParams exmy_params(int f) {
     const int bias = (1 << (e - 1)) - 1;
     p.emin = 1 - bias;
     p.emax = ((1 << e) - 1) - bias;
-    p.maxf = ldexpf(2.0f - ldexpf(1.0f, -m), p.emax);
+    // e8m0's largest magnitude, 2^128, is beyond fp32: its kernels clamp
+    // half the scaled magnitude, at 2^127
+    p.maxf = e == 8 ? ldexpf(1.0f, 127) : ldexpf(2.0f - ldexpf(1.0f, -m), p.emax);
   } else {
     p.emin = m;
     p.emax = m - 1;

@@ -12,7 +12,7 @@ namespace mxk {
 // Generic eXmY format parameters (prepared on the host): m mantissa bits;
 // emin = exponent of the smallest normal (m for integer formats); emax =
 // floor(log2 of the largest magnitude); bias = 1 - emin; maxf = the largest
-// magnitude; dec_bits, dec_sub as below.
+// magnitude (e8m0: half of it, 2^127); dec_bits, dec_sub as below.
 struct ExmyParams {
   int m;
   int emin;

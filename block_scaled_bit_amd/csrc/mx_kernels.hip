@@ -553,6 +553,27 @@ __device__ __forceinline__ uint32_t exmy_round(float a, const ExmyParams& p) {
   return mag;
 }
 
+// e8m0 (exponent only: zero and 2^-126 .. 2^128).  A block's top binade of
+// scaled values, [2^128, 2^129), lies beyond fp32, so its codes come from h =
+// a / 2 = |v| 2^(126 - byte), clamped to 2^127 (p.maxf).  The scaling is
+// exact: a finite block has byte <= 126, so it never shifts a bit out.
+// Magnitude code k >= 1 is h = 2^(k - 128).  A normal h = 2^(F - 127) (1 +
+// M 2^-23) lies between codes F + 1 and F + 2, its midpoint at M = 2^22 going
+// to the even code; an fp32-subnormal h is compared with the midpoints 2^-128
+// (codes 0 and 1) and 1.5 2^-127 (codes 1 and 2), ties to the even code.
+__device__ __forceinline__ uint32_t e8m0_code_of_half(float h) {
+  const uint32_t b = __float_as_uint(h), F = b >> 23, M = b & 0x7FFFFFu;
+  const uint32_t up = (M > 0x400000u) | ((M == 0x400000u) & ((F + 1u) & 1u));
+  const uint32_t sub = M <= 0x200000u ? 0u : (M < 0x600000u ? 1u : 2u);
+  return F ? F + 1u + up : sub;
+}
+
+// e8m0's magnitude code k times 2^scale_exp: 2^(k - 127 + scale_exp), rounded
+// by ldexp (to inf above fp32, to a subnormal or zero below it); code 0 is 0.
+__device__ __forceinline__ float e8m0_decode(uint32_t mag, int scale_exp) {
+  return mag ? __builtin_ldexpf(1.0f, (int)mag - 127 + scale_exp) : 0.0f;
+}
+
 __device__ __forceinline__ uint32_t exmy_byte_from_amax(uint32_t amax, const ExmyParams& p) {
   if (amax >= 0x7F800000u) return 0xFFu;
   if (amax == 0u) return 0u;
@@ -584,6 +605,15 @@ __device__ __forceinline__ void exmy_codes(const uint32_t (&v)[32], uint32_t byt
                                            const ExmyParams& p, uint32_t (&c)[32]) {
   // a poisoned block (byte 0xFF) gives arbitrary codes here; the callers
   // zero them
+  if constexpr (W == 9 && M0) {  // e8m0
+    const int sh = 126 - (int)byte;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float h = fminf(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(v[k])), sh), p.maxf);
+      c[k] = e8m0_code_of_half(h) | ((v[k] >> 31) << 8);
+    }
+    return;
+  }
   const int neg_exp = 127 - (int)byte;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
@@ -591,6 +621,13 @@ __device__ __forceinline__ void exmy_codes(const uint32_t (&v)[32], uint32_t byt
         fminf(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(v[k])), neg_exp), p.maxf);
     c[k] = exmy_round<M0>(a, p) | ((v[k] >> 31) << (W - 1));
   }
+}
+
+// The value of a magnitude code times 2^scale_exp, for any split.
+template <bool E8>
+__device__ __forceinline__ float exmy_value(uint32_t mag, int scale_exp, const ExmyParams& p) {
+  if constexpr (E8) return e8m0_decode(mag, scale_exp);
+  return exmy_decode(mag, scale_exp, p);
 }
 
 template <int W, bool BF16, bool M0>
@@ -638,7 +675,7 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
     const int sexp = (int)byte - 127;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const float val = exmy_decode(c[k] & ((1u << (W - 1)) - 1u), sexp, p);  // exact
+      const float val = exmy_value<W == 9 && M0>(c[k] & ((1u << (W - 1)) - 1u), sexp, p);
       out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(val) | (v[k] & 0x80000000u));
     }
     if constexpr (BF16) {
@@ -656,7 +693,7 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
   }
 }
 
-template <int W, bool BF16>
+template <int W, bool BF16, bool E8>
 __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        int64_t nb, void* __restrict__ y,
@@ -679,7 +716,7 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const uint32_t code = unpack1<W>(o, k);
-      const float val = exmy_decode(code & ((1u << (W - 1)) - 1u), sexp, p);
+      const float val = exmy_value<E8>(code & ((1u << (W - 1)) - 1u), sexp, p);
       out[k] = __float_as_uint(val) | ((code >> (W - 1)) << 31);
     }
     if (byte == 0xFFu) {  // rare: a poisoned block
@@ -1044,7 +1081,8 @@ hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const 
                        hipStream_t st) {
   const dim3 block(256);
   const dim3 grid = (op == 0) ? grid_for(nb, 256) : grid_for(nb, 4 * kTile);
-  // exponent-only formats (m = 0) need the even-exponent tie rule
+  // exponent-only formats (m = 0) need the even-exponent tie rule; width 9
+  // with m = 0 is e8m0, which has code paths of its own
 #define MXK_EXMY_LAUNCH(M0)                                                                     \
   MXK_SWITCH_WIDTH(width, {                                                                     \
     if (op == 0) {                                                                              \
@@ -1056,10 +1094,10 @@ hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const 
                            (uint32_t*)out, scales_out, p);                                      \
     } else if (op == 1) {                                                                       \
       if (bf16)                                                                                 \
-        hipLaunchKernelGGL((dequantize_exmy<WW, true>), grid, block, 0, st,                     \
+        hipLaunchKernelGGL((dequantize_exmy<WW, true, M0 && WW == 9>), grid, block, 0, st,      \
                            (const uint32_t*)in, scales_in, nb, out, p);                         \
       else                                                                                      \
-        hipLaunchKernelGGL((dequantize_exmy<WW, false>), grid, block, 0, st,                    \
+        hipLaunchKernelGGL((dequantize_exmy<WW, false, M0 && WW == 9>), grid, block, 0, st,     \
                            (const uint32_t*)in, scales_in, nb, out, p);                         \
     } else {                                                                                    \
       if (bf16)                                                                                 \

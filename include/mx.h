@@ -82,11 +82,14 @@ typedef enum {
 
 /* Generic eXmY formats ("eXmY" abstract: every split of a bit width into
  * exponent and mantissa bits): identifier 0x100 | e << 4 | m, width
- * w = 1 + e + m between 3 and 9 bits, e <= 7.  Sign-magnitude codes with
- * IEEE-style fields (bias 2^(e-1) - 1, subnormals) and no special codes;
- * e = 0 is an integer magnitude 0 .. 2^m - 1.  Scale byte as above with
- * emax = floor(log2 of the largest magnitude); ties go to the even code
- * (for m = 0 that is the even exponent field).  Codes pack like the other
+ * w = 1 + e + m between 3 and 9 bits (so e <= 8; all 42 splits).
+ * Sign-magnitude codes with IEEE-style fields (bias 2^(e-1) - 1,
+ * subnormals) and no special codes; e = 0 is an integer magnitude
+ * 0 .. 2^m - 1.  Scale byte as above with emax = floor(log2 of the largest
+ * magnitude); ties go to the even code (for m = 0 that is the even
+ * exponent field).  e8m0 holds zero and 2^-126 .. 2^128: its dequantized
+ * values overflow to inf or round to subnormals and zero as the exact
+ * product demands.  Codes pack like the other
  * formats: 32 codes of w bits = 4w bytes per block.  AXS-6 equals e0m5
  * with its scale byte 4 higher (where neither byte is clamped).  Not
  * accepted by mx_softmax_quantize. */

@@ -196,7 +196,9 @@ def test_python_helpers_check_every_buffer_before_launching(mx):
 def test_generic_exmy_formats_host_checks(mx):
     assert mx.mx_buffer_sizes(mx.MX_EXMY(3, 3), 32, 4, 64) == (4 * 2 * 28, 8, 0)
     assert mx.mx_buffer_sizes("e0m8", 32, 1, 32) == (36, 1, 0)
-    for bad in (mx.MX_EXMY(8, 0), mx.MX_EXMY(0, 1), mx.MX_EXMY(1, 0), mx.MX_EXMY(4, 5), 0x200):
+    assert mx.mx_buffer_sizes(mx.MX_EXMY(8, 0), 32, 2, 64) == (2 * 2 * 36, 4, 0)
+    for bad in (mx.MX_EXMY(8, 1), mx.MX_EXMY(9, 0), mx.MX_EXMY(0, 1), mx.MX_EXMY(1, 0),
+                mx.MX_EXMY(4, 5), 0x200):
         assert mx.mx_quantize(bad, 32, 0, A, 4, 32, A, A, None, stream=0) == UNSUP
     assert mx.mx_softmax_quantize(mx.MX_EXMY(2, 1), 32, A, 4, 32, A, A, stream=0) == UNSUP
     assert mx.mx_quantize(mx.MX_EXMY(2, 2), 32, 0, None, 4, 32, A, A, None, stream=0) == NULL

@@ -81,13 +81,15 @@ def test_every_bf16_pattern_and_every_tie(mx, fmt):
     oc, os_, _ = oracle.quantize(fmt, x)
     assert_bytes_equal(to_host(scales), os_, "scales")
     assert_bytes_equal(to_host(codes), oc, "codes", oracle.BYTES_PER_BLOCK[fmt])
-    # fp32 midpoints between neighbouring grid values, and their neighbours
-    g = brute.finite_grid(fmt)
+    # fp32 midpoints between neighbouring grid values, and their neighbours,
+    # under X = 2^-sh (e8m0's grid reaches 2^128; half of it fits fp32)
+    sh = max(0, brute.emax(fmt) - 127)
+    g = brute.finite_grid(fmt) * 2.0 ** -sh
     mids = ((g[:-1] + g[1:]) / 2.0).astype(np.float32)
     vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e30)), -mids])
     nblk = (len(vals) + 30) // 31
     t = np.empty((nblk, 32), np.float32)
-    t[:, 0] = np.float32(2.0 ** brute.emax(fmt))
+    t[:, 0] = np.float32(2.0 ** (brute.emax(fmt) - sh))
     t[:, 1:] = np.resize(vals, nblk * 31).reshape(nblk, 31)
     codes, scales, _ = mx.quantize(to_dev(t), fmt)
     torch.cuda.synchronize()
