@@ -5,11 +5,13 @@
 // magnitude in registers, derives the shared scale byte, converts the 32
 // values with the scaled-convert instructions (FP6: one 32-wide instruction;
 // FP4/FP8: one per pair) or, for AXS-6, with integer/fp32 arithmetic, and
-// writes its packed codes (24/16/32 B) and its scale byte.  No value crosses
-// lanes, so every output byte has exactly one writer and in-place
-// fake-quantization is safe (a lane reads its block before writing it).
-// The exp-then-quantize kernel is the exception: there two lanes share a
-// block (see its section below).
+// writes its packed codes (24/16/32 B) and its scale byte.  No arithmetic
+// crosses lanes, so every output byte has exactly one writer.  Wide outputs
+// (and the bf16 fake-quantize inputs) pass through a per-wave LDS tile of 64
+// blocks for coalesced 1 KB accesses; a wave has read its whole tile before
+// it writes any of it, so in-place fake-quantization is safe.  The
+// exp-then-quantize kernel is the exception: there two lanes share a block
+// (see its section below).
 //
 // Rules: "Online MXFP6" page ("Start a model": packed codes and an E8M0
 // scale per 32 values); "EFQ-Softmax" explainer (exponent-only block scale
