@@ -114,12 +114,14 @@ def _smi_clock_doc(text):
     raise ValueError("no clock list in the output")
 
 
-def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
+def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3, lead_s=1.0):
     """The GPU's clocks as amd-smi reports them while `step` (the headline
     kernel) runs back to back: per sample the mean, lowest and highest of
     the eight XCDs' graphics clocks, the memory clock and the rated
-    maximum, in MHz.  None when the tool is missing; a sample that fails
-    records the error.  Reported beside the timing, never used by it."""
+    maximum, in MHz, and the seconds since the load started.  The first
+    sample waits lead_s so the clocks have left any idle state.  None when
+    the tool is missing; a sample that fails records the error.  Reported
+    beside the timing, never used by it."""
     import shutil
     import subprocess
     import threading
@@ -136,9 +138,13 @@ def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
             cmd = [sys.executable, exe]
     readings = []
 
+    t_start = time.perf_counter()
+
     def sample():
+        time.sleep(lead_s)
         for _ in range(samples):
             time.sleep(seconds / (samples + 1))
+            t_at = round(time.perf_counter() - t_start, 2)
             try:
                 r = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True,
                                    text=True, timeout=10)
@@ -147,7 +153,8 @@ def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
                 readings.append({"gfx_mean_MHz": round(sum(gfx) / len(gfx)),
                                  "gfx_min_MHz": min(gfx), "gfx_max_MHz": max(gfx),
                                  "mem_MHz": c.get("mem_0", {}).get("clk", {}).get("value"),
-                                 "gfx_rated_max_MHz": c["gfx_0"]["max_clk"]["value"]})
+                                 "gfx_rated_max_MHz": c["gfx_0"]["max_clk"]["value"],
+                                 "s_under_load": t_at})
             except Exception as e:  # a reading, not a measurement: never fatal
                 readings.append({"error": type(e).__name__})
 
@@ -155,7 +162,7 @@ def gpu_clocks_under_load(step, nsets, seconds=1.5, samples=3):
     th.start()
     i = 0
     while th.is_alive():
-        for _ in range(64):
+        for _ in range(256):  # ~8 ms of work queued between host waits
             step(i % nsets)
             i += 1
         torch.cuda.synchronize()
