@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 5
+#define MX_ABI_VERSION 6
 #define MX_BLOCK 32
 
 typedef enum {
@@ -82,7 +82,8 @@ typedef enum {
 
 /* Generic eXmY formats ("eXmY" abstract: every split of a bit width into
  * exponent and mantissa bits): identifier 0x100 | e << 4 | m, width
- * w = 1 + e + m between 3 and 9 bits (so e <= 8; all 42 splits).
+ * w = 1 + e + m between 3 and 9 bits (so e <= 8; all 42 splits; e8m0
+ * from ABI version 6).
  * Sign-magnitude codes with IEEE-style fields (bias 2^(e-1) - 1,
  * subnormals) and no special codes; e = 0 is an integer magnitude
  * 0 .. 2^m - 1.  Scale byte as above with emax = floor(log2 of the largest

@@ -51,7 +51,7 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 5
+    assert mx.mx_abi_version() == 6
     for s in range(0, 8):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
