@@ -254,11 +254,12 @@ def rows_floor_probe():
 # access schedules of the byte-mix copy (tests/hwprobe/bw_probe.hip)
 MIX_VARIANTS = {0: "quantizer_grid", 1: "xcd_contiguous", 2: "read_phase_then_write_4_blocks",
                 3: "read_phase_then_write_4_blocks_xcd", 7: "nontemporal_stores",
-                11: "coalesced_1KB_instructions", 4: "reads_only", 5: "writes_only",
+                11: "coalesced_1KB_instructions", 12: "lds_1KB_loads_lane_stores",
+                4: "reads_only", 5: "writes_only",
                 10: "reads_only_coalesced", 9: "writes_only_coalesced"}
 MIX_COPIES = ("quantizer_grid", "xcd_contiguous", "read_phase_then_write_4_blocks",
               "read_phase_then_write_4_blocks_xcd", "nontemporal_stores",
-              "coalesced_1KB_instructions")
+              "coalesced_1KB_instructions", "lds_1KB_loads_lane_stores")
 
 
 def mix_variant_probe():

@@ -105,6 +105,10 @@ extern "C" int probe_rows_floor(const void* s, int64_t rows, int64_t cols, void*
 //   variants 9, 10, 11  writes only, reads only, and the whole mix, with
 //              every instruction of a wave covering 1 KB of consecutive
 //              bytes (whole workgroups of 256 blocks only)
+//   variant 12 the bf16 quantizers' schedule: a wave's 64 blocks (4 KB)
+//              reach LDS by four direct global->LDS loads of 1 KB each,
+//              then every lane reads its block from LDS and stores like
+//              variant 0 (whole waves only)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t xcd_order(int64_t wg, int64_t total) {
   return (total & 7) == 0 ? (wg & 7) * (total >> 3) + (wg >> 3) : wg;
@@ -239,6 +243,43 @@ __global__ __launch_bounds__(256) void mix_coalesced(const uint4* __restrict__ x
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glob_void_t;
+
+// 16-byte quarter q of tile block b sits in LDS slot 4b + (q ^ ((b / 4) % 4)),
+// so the 16 lanes of one LDS read cycle hit 16 distinct slots; the map is
+// its own inverse, so lane l of load i fetches the piece slot 64 i + l holds
+__device__ __forceinline__ int tile_slot(int b, int q) { return 4 * b + (q ^ ((b >> 2) & 3)); }
+
+__global__ __launch_bounds__(256) void mix_lds_loads(const uint4* __restrict__ x, int64_t nb,
+                                                     uint64_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
+  __shared__ uint4 tile[4][256];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (b0 + 64 > nb) return;  // whole waves only (timing probe)
+  const uint4* src = x + 4 * b0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int S = 64 * i + lane;
+    __builtin_amdgcn_global_load_lds((glob_void_t*)(src + tile_slot(S >> 2, S & 3)),
+                                     (lds_void_t*)(&tile[wave][64 * i]), 16, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint4 q0 = tile[wave][tile_slot(lane, 0)], q1 = tile[wave][tile_slot(lane, 1)];
+  const uint4 q2 = tile[wave][tile_slot(lane, 2)], q3 = tile[wave][tile_slot(lane, 3)];
+  const int64_t b = b0 + lane;
+  const uint32_t o0 = q0.x ^ q2.z, o1 = q0.y ^ q2.w, o2 = q0.z ^ q3.x, o3 = q0.w ^ q3.y;
+  const uint32_t o4 = q1.x ^ q1.z ^ q3.z, o5 = q1.y ^ q1.w ^ q3.w ^ q2.x ^ q2.y;
+  codes[3 * b] = o0 | ((uint64_t)o1 << 32);
+  codes[3 * b + 1] = o2 | ((uint64_t)o3 << 32);
+  codes[3 * b + 2] = o4 | ((uint64_t)o5 << 32);
+  scales[b] = (uint8_t)(o0 ^ o5);
+}
+
 // variant as above; x: nb * 64 bytes, codes: nb * 24 bytes (16-byte
 // aligned), scales: nb bytes, sink: at least ceil(nb / 256) dwords (variant 4
 // only).  Returns hipGetLastError(), or -1 for an unknown variant.
@@ -296,6 +337,10 @@ extern "C" int probe_mix_variant(int variant, const void* x, int64_t nb, void* c
     case 11:
       hipLaunchKernelGGL((mix_coalesced<true, true>), dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
                          static_cast<uint4*>(codes), reinterpret_cast<uint4*>(scales), sink);
+      break;
+    case 12:
+      hipLaunchKernelGGL(mix_lds_loads, dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales);
       break;
     default: return -1;
   }
