@@ -252,14 +252,16 @@ def rows_floor_probe():
 
 
 # access schedules of the byte-mix copy (tests/hwprobe/bw_probe.hip)
-MIX_VARIANTS = {0: "quantizer_grid", 1: "xcd_contiguous", 2: "read_phase_then_write_4_blocks",
-                3: "read_phase_then_write_4_blocks_xcd", 7: "nontemporal_stores",
-                11: "coalesced_1KB_instructions", 12: "lds_1KB_loads_lane_stores",
-                4: "reads_only", 5: "writes_only",
-                10: "reads_only_coalesced", 9: "writes_only_coalesced"}
-MIX_COPIES = ("quantizer_grid", "xcd_contiguous", "read_phase_then_write_4_blocks",
-              "read_phase_then_write_4_blocks_xcd", "nontemporal_stores",
-              "coalesced_1KB_instructions", "lds_1KB_loads_lane_stores")
+MIX_VARIANTS = {12: "quantizer_grid", 0: "lane_16B_loads", 1: "xcd_contiguous",
+                2: "read_phase_then_write_4_blocks", 3: "read_phase_then_write_4_blocks_xcd",
+                7: "nontemporal_stores", 11: "coalesced_1KB_instructions",
+                4: "reads_only", 5: "writes_only", 10: "reads_only_coalesced",
+                9: "writes_only_coalesced", 13: "reads_only_lds"}
+MIX_COPIES = ("quantizer_grid", "lane_16B_loads", "xcd_contiguous",
+              "read_phase_then_write_4_blocks", "read_phase_then_write_4_blocks_xcd",
+              "nontemporal_stores", "coalesced_1KB_instructions")
+MIX_READS = ("reads_only", "reads_only_coalesced", "reads_only_lds")
+MIX_WRITES = ("writes_only", "writes_only_coalesced")
 
 
 def mix_variant_probe():
@@ -829,8 +831,9 @@ def main():
     }
     if sched:
         best = min(MIX_COPIES, key=lambda k: sched[k])
-        serial = min(sched["reads_only"], sched["reads_only_coalesced"]) + \
-            min(sched["writes_only"], sched["writes_only_coalesced"])
+        rd = min(sched[k] for k in MIX_READS)
+        wr = min(sched[k] for k in MIX_WRITES)
+        serial = rd + wr
         out["best_mix_ceiling"] = {
             "us": round(sched[best] * 1e3, 3), "schedule": best,
             "frac_of_peak": round(alg_b / sched[best] / 1e6 / HBM_PEAK_GBS, 4),
@@ -838,10 +841,8 @@ def main():
             "schedules_us": {k: round(v * 1e3, 3) for k, v in sched.items()},
             "serial_bound_us": round(serial * 1e3, 3),
             "serial_bound_frac_of_peak": round(alg_b / serial / 1e6 / HBM_PEAK_GBS, 4),
-            "read_only_GBps": round(in_b / min(sched["reads_only"],
-                                               sched["reads_only_coalesced"]) / 1e6, 1),
-            "write_only_GBps": round((alg_b - in_b) / min(sched["writes_only"],
-                                                          sched["writes_only_coalesced"]) / 1e6, 1),
+            "read_only_GBps": round(in_b / rd / 1e6, 1),
+            "write_only_GBps": round((alg_b - in_b) / wr / 1e6, 1),
             "note": "copy kernels moving the quantizer's bytes with no arithmetic, in each access "
                     "schedule (tests/hwprobe/bw_probe.hip), same buffers, rotation, warm-up and "
                     "steps; serial bound = the fastest reads alone plus the fastest writes alone"}

@@ -1,12 +1,12 @@
 // bw_probe.hip -- the HBM ceiling of the bf16 -> FP6 quantizer's byte mix.
 //
-// A copy kernel with the quantizer's layout, grid and memory instructions
-// (one lane per 32-value block: four 16-byte loads of its 64 bf16 bytes,
-// three 8-byte stores of 24 "code" bytes, one scale byte) and no
-// arithmetic beyond folding every input word into the outputs, so that the
-// compiler keeps every load.  The benchmark times it beside the quantizer
-// on the same buffers; it is measurement infrastructure, not part of the
-// library.
+// Copy kernels that move the quantizer's bytes in several access schedules
+// with no arithmetic beyond folding every input word into the outputs, so
+// that the compiler keeps every load; the first (mix_copy) has one lane per
+// 32-value block doing four 16-byte loads of its 64 bf16 bytes, three
+// 8-byte stores of 24 "code" bytes and one scale byte.  The benchmark times
+// them beside the quantizer on the same buffers; this is measurement
+// infrastructure, not part of the library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -87,7 +87,7 @@ extern "C" int probe_rows_floor(const void* s, int64_t rows, int64_t cols, void*
 // ---------------------------------------------------------------------------
 // Other access schedules for the same byte mix (64 bytes read, 24 + 1
 // written per 32-value block), to find the fastest one this HBM allows:
-//   variant 0  the quantizer's schedule (mix_copy above)
+//   variant 0  one lane per block with direct 16-byte loads (mix_copy above)
 //   variant 1  the same, with workgroups renumbered so that each of the 8
 //              XCDs (which receive consecutive workgroups in turn) covers
 //              one contiguous eighth of the tensor
@@ -105,10 +105,11 @@ extern "C" int probe_rows_floor(const void* s, int64_t rows, int64_t cols, void*
 //   variants 9, 10, 11  writes only, reads only, and the whole mix, with
 //              every instruction of a wave covering 1 KB of consecutive
 //              bytes (whole workgroups of 256 blocks only)
-//   variant 12 the bf16 quantizers' schedule: a wave's 64 blocks (4 KB)
+//   variant 12 the bf16 MX quantizer's schedule: a wave's 64 blocks (4 KB)
 //              reach LDS by four direct global->LDS loads of 1 KB each,
 //              then every lane reads its block from LDS and stores like
 //              variant 0 (whole waves only)
+//   variant 13 the loads of variant 12 alone (one dword written per wave)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t xcd_order(int64_t wg, int64_t total) {
   return (total & 7) == 0 ? (wg & 7) * (total >> 3) + (wg >> 3) : wg;
@@ -251,9 +252,11 @@ typedef __attribute__((address_space(1))) const void glob_void_t;
 // its own inverse, so lane l of load i fetches the piece slot 64 i + l holds
 __device__ __forceinline__ int tile_slot(int b, int q) { return 4 * b + (q ^ ((b >> 2) & 3)); }
 
+template <bool WRITE>
 __global__ __launch_bounds__(256) void mix_lds_loads(const uint4* __restrict__ x, int64_t nb,
                                                      uint64_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scales) {
+                                                     uint8_t* __restrict__ scales,
+                                                     uint32_t* __restrict__ sink) {
   __shared__ uint4 tile[4][256];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
@@ -274,15 +277,21 @@ __global__ __launch_bounds__(256) void mix_lds_loads(const uint4* __restrict__ x
   const int64_t b = b0 + lane;
   const uint32_t o0 = q0.x ^ q2.z, o1 = q0.y ^ q2.w, o2 = q0.z ^ q3.x, o3 = q0.w ^ q3.y;
   const uint32_t o4 = q1.x ^ q1.z ^ q3.z, o5 = q1.y ^ q1.w ^ q3.w ^ q2.x ^ q2.y;
-  codes[3 * b] = o0 | ((uint64_t)o1 << 32);
-  codes[3 * b + 1] = o2 | ((uint64_t)o3 << 32);
-  codes[3 * b + 2] = o4 | ((uint64_t)o5 << 32);
-  scales[b] = (uint8_t)(o0 ^ o5);
+  if constexpr (WRITE) {
+    codes[3 * b] = o0 | ((uint64_t)o1 << 32);
+    codes[3 * b + 1] = o2 | ((uint64_t)o3 << 32);
+    codes[3 * b + 2] = o4 | ((uint64_t)o5 << 32);
+    scales[b] = (uint8_t)(o0 ^ o5);
+  } else {
+    // a store that depends on every loaded word keeps every load alive
+    const uint32_t acc = o0 ^ o1 ^ o2 ^ o3 ^ o4 ^ o5 ^ q0.x ^ q2.x ^ q2.y;
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+  }
 }
 
 // variant as above; x: nb * 64 bytes, codes: nb * 24 bytes (16-byte
-// aligned), scales: nb bytes, sink: at least ceil(nb / 256) dwords (variant 4
-// only).  Returns hipGetLastError(), or -1 for an unknown variant.
+// aligned), scales: nb bytes, sink: at least ceil(nb / 256) dwords (variants
+// 4, 10 and 13).  Returns hipGetLastError(), or -1 for an unknown variant.
 extern "C" int probe_mix_variant(int variant, const void* x, int64_t nb, void* codes,
                                  uint8_t* scales, uint32_t* sink, void* stream) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -339,8 +348,12 @@ extern "C" int probe_mix_variant(int variant, const void* x, int64_t nb, void* c
                          static_cast<uint4*>(codes), reinterpret_cast<uint4*>(scales), sink);
       break;
     case 12:
-      hipLaunchKernelGGL(mix_lds_loads, dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
-                         static_cast<uint64_t*>(codes), scales);
+      hipLaunchKernelGGL(mix_lds_loads<true>, dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales, sink);
+      break;
+    case 13:
+      hipLaunchKernelGGL(mix_lds_loads<false>, dim3((unsigned)g1), dim3(256), 0, st, xi, nb,
+                         static_cast<uint64_t*>(codes), scales, sink);
       break;
     default: return -1;
   }
