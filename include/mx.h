@@ -123,7 +123,8 @@ mx_status mx_buffer_sizes(mx_format fmt, int block, int64_t rows, int64_t cols,
 
 /* Quantize + pack ("Online MXFP6", "Start a model": replace a tensor by
  * packed codes plus one scale per 32 values).  x: [rows, cols] of in_dtype.
- * Writes codes, scales and (AXS-6) aux; every byte of them is written. */
+ * Writes codes, scales and (AXS-6) aux; every byte of them is written.
+ * The outputs must not overlap x or one another. */
 mx_status mx_quantize(mx_format fmt, int block, mx_dtype in_dtype,
                       const void *x, int64_t rows, int64_t cols, void *codes,
                       uint8_t *scales, uint8_t *aux, void *stream);
