@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 FP6_E2M3, FP6_E3M2, FP4_E2M1, FP8_E4M3, AXS6 = 0, 1, 2, 3, 4
-BF16, FP32 = 0, 1
+BF16, FP32, F16 = 0, 1, 2
 BLOCK = 32
 NAMES = {"mxfp6_e2m3": FP6_E2M3, "mxfp6_e3m2": FP6_E3M2, "mxfp4": FP4_E2M1,
          "mxfp8": FP8_E4M3, "axs6": AXS6}
@@ -108,7 +108,12 @@ def _dtype_of(x: np.ndarray) -> int:
         return BF16
     if x.dtype == np.float32:
         return FP32
-    raise TypeError(f"oracle input must be uint16 (bf16 bits) or float32, got {x.dtype}")
+    if x.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle input must be uint16 (bf16 bits), float32 or float16, got {x.dtype}")
+
+
+_OUT_NP = {BF16: np.uint16, FP32: np.float32, F16: np.float16}
 
 
 def _rows_cols(x: np.ndarray):
@@ -163,7 +168,7 @@ def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, aux, rows: int, 
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     auxa = np.ascontiguousarray(aux if aux is not None and len(aux) else np.zeros(1, np.uint8),
                                 dtype=np.uint8)
-    y = np.empty((rows, cols), np.uint16 if out_dtype == BF16 else np.float32)
+    y = np.empty((rows, cols), _OUT_NP[out_dtype])
     rc = _lib.mxref_dequantize(fmt, BLOCK, _ptr(codes), _ptr(scales), _ptr(auxa), rows, cols,
                                out_dtype, _ptr(y))
     if rc:

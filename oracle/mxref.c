@@ -254,11 +254,27 @@ static void unpack_block(const fmt_t *f, const uint8_t *in, int *c) {
 }
 
 /* ------------------------------------------------------------------ */
-/* Host number formats: bf16 = top half of an fp32 bit pattern.         */
+/* Host number formats: bf16 = top half of an fp32 bit pattern; fp16 =  */
+/* IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 mantissa     */
+/* bits, subnormals), the other source type the [MXFP6] page names      */
+/* ("Start a model": BF16 or FP16 weights).                             */
 /* ------------------------------------------------------------------ */
+static double half_to_double(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -24);          /* m * 2^-24 */
+  else
+    v = ldexp(1024.0 + m, e - 25);      /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
 static double load_value(int dtype, const void *x, int64_t i) {
   uint32_t u;
   float fv;
+  if (dtype == MXREF_F16) return half_to_double(((const uint16_t *)x)[i]);
   if (dtype == MXREF_BF16)
     u = (uint32_t)((const uint16_t *)x)[i] << 16;
   else
@@ -296,8 +312,33 @@ static uint32_t round_to_bits(double y, int p) {
   return sign | (field << 23) | (mant << (24 - p));
 }
 
+/* Round a double to binary16 (11 significand bits, normal exponents
+ * -14..15), round-to-nearest-even, gradual underflow down to 2^-24,
+ * overflow to infinity; NaN -> the canonical quiet NaN 0x7E00. */
+static uint16_t round_to_half(double y) {
+  const uint16_t sign = signbit(y) ? 0x8000u : 0u;
+  double ay = fabs(y), r;
+  int e, q;
+  if (isnan(y)) return 0x7E00u;
+  if (ay == 0.0) return sign;
+  if (isinf(y)) return (uint16_t)(sign | 0x7C00u);
+  e = ilog2(ay);
+  q = (e > -14 ? e : -14) - 10; /* exponent of one ulp */
+  r = nearbyint(ay / ldexp(1.0, q)) * ldexp(1.0, q);
+  if (r >= 65536.0) return (uint16_t)(sign | 0x7C00u);
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+  {
+    int er = ilog2(r);
+    uint16_t field = (uint16_t)(er + 15);
+    uint16_t mant = (uint16_t)((r / ldexp(1.0, er) - 1.0) * 1024.0);
+    return (uint16_t)(sign | (field << 10) | mant);
+  }
+}
+
 static void store_value(int dtype, void *y, int64_t i, double v) {
-  if (dtype == MXREF_BF16) {
+  if (dtype == MXREF_F16) {
+    ((uint16_t *)y)[i] = round_to_half(v);
+  } else if (dtype == MXREF_BF16) {
     uint32_t u = round_to_bits(v, 8);
     ((uint16_t *)y)[i] = (uint16_t)(u >> 16);
   } else {
@@ -322,6 +363,8 @@ static int quantize_values(const fmt_t *f, int fmt, const double *v, int *c) {
   return byte;
 }
 
+static int dtype_ok(int d) { return d == MXREF_BF16 || d == MXREF_FP32 || d == MXREF_F16; }
+
 int mxref_quantize(int fmt, int block, int in_dtype, const void *x,
                    int64_t rows, int64_t cols, uint8_t *codes,
                    uint8_t *scales, uint8_t *aux) {
@@ -330,7 +373,7 @@ int mxref_quantize(int fmt, int block, int in_dtype, const void *x,
   int64_t nb, b;
   double v[BLOCK];
   int c[BLOCK], k;
-  if (check_args(fmt, block, rows, cols)) return -1;
+  if (check_args(fmt, block, rows, cols) || !dtype_ok(in_dtype)) return -1;
   nb = rows * (cols / BLOCK);
   for (b = 0; b < nb; b++) {
     for (k = 0; k < BLOCK; k++) v[k] = load_value(in_dtype, x, b * BLOCK + k);
@@ -356,7 +399,7 @@ int mxref_dequantize(int fmt, int block, const uint8_t *codes,
   const fmt_t *f = get_fmt(fmt, &fs) ? &fs : 0;
   int64_t nb, b;
   int c[BLOCK], k;
-  if (check_args(fmt, block, rows, cols)) return -1;
+  if (check_args(fmt, block, rows, cols) || !dtype_ok(out_dtype)) return -1;
   nb = rows * (cols / BLOCK);
   for (b = 0; b < nb; b++) {
     int byte = scales[b];
@@ -385,7 +428,7 @@ int mxref_fake_quantize(int fmt, int block, int dtype, const void *x, void *y,
   int64_t nb, b;
   double v[BLOCK];
   int c[BLOCK], k, byte;
-  if (check_args(fmt, block, rows, cols)) return -1;
+  if (check_args(fmt, block, rows, cols) || !dtype_ok(dtype)) return -1;
   nb = rows * (cols / BLOCK);
   for (b = 0; b < nb; b++) {
     for (k = 0; k < BLOCK; k++) v[k] = load_value(dtype, x, b * BLOCK + k);

@@ -33,7 +33,7 @@ extern "C" {
 
 enum { MXREF_FP6_E2M3 = 0, MXREF_FP6_E3M2 = 1, MXREF_FP4_E2M1 = 2,
        MXREF_FP8_E4M3 = 3, MXREF_AXS6 = 4 };
-enum { MXREF_BF16 = 0, MXREF_FP32 = 1 };
+enum { MXREF_BF16 = 0, MXREF_FP32 = 1, MXREF_F16 = 2 };
 /* return codes: 0 ok, -1 bad argument */
 
 int    mxref_bytes_per_block(int fmt);
