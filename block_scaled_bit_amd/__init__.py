@@ -17,6 +17,7 @@ import torch  # noqa: F401  (loads the HIP runtime that libmx.so binds to)
 
 __all__ = [
     "MX_FP6_E2M3", "MX_FP6_E3M2", "MX_FP4_E2M1", "MX_FP8_E4M3", "MX_AXS6", "MX_BF16", "MX_FP32",
+    "MX_FP16",
     "FORMATS", "MX_EXMY", "MxError", "mx_abi_version", "mx_status_str", "mx_buffer_sizes", "mx_quantize",
     "mx_quantize_batch", "quantize_many", "mx_dequantize", "mx_fake_quantize", "mx_softmax_quantize", "mx_attention_fwd",
     "mx_attention_fwd_efq", "quantize",
@@ -25,7 +26,7 @@ __all__ = [
 ]
 
 MX_FP6_E2M3, MX_FP6_E3M2, MX_FP4_E2M1, MX_FP8_E4M3, MX_AXS6 = 0, 1, 2, 3, 4
-MX_BF16, MX_FP32 = 0, 1
+MX_BF16, MX_FP32, MX_FP16 = 0, 1, 2
 BLOCK = 32
 
 
@@ -204,6 +205,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return MX_BF16
     if t.dtype == torch.float32:
         return MX_FP32
+    if t.dtype == torch.float16:
+        return MX_FP16
     raise MxError(4, f"dtype {t.dtype}")
 
 
@@ -311,7 +314,7 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, aux=None, fmt="mxfp6_e
     _need(codes, "codes", torch.uint8, nb * BYTES_PER_BLOCK[f])
     if f == MX_AXS6:
         _need(aux, "aux", torch.uint8, (nb + 3) // 4)
-    if out_dtype not in (torch.bfloat16, torch.float32):
+    if out_dtype not in (torch.bfloat16, torch.float32, torch.float16):
         raise MxError(4, f"dtype {out_dtype}")
     _on_gpu(scales, "scales")
     _on_gpu(codes, "codes", scales)

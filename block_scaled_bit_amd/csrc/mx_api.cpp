@@ -47,7 +47,7 @@ mxk::ExmyParams exmy_params(int f) {
   p.dec_sub = -ldexpf(1.0f, 1 - p.bias);
   return p;
 }
-bool dtype_ok(int d) { return d == MX_BF16 || d == MX_FP32; }
+bool dtype_ok(int d) { return d == MX_BF16 || d == MX_FP32 || d == MX_FP16; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Common shape / format checks.  Sets *nothing = true for an empty tensor.
@@ -129,9 +129,9 @@ hipError_t quantize_one(int fmt, int in_dtype, const void* x, int64_t rows, int6
                         void* codes, uint8_t* scales, uint8_t* aux, hipStream_t st) {
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
-    return mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype == MX_BF16, x,
+    return mxk::launch_exmy(0, exmy_width(fmt), exmy_params(fmt), in_dtype, x,
                             nullptr, nb, codes, scales, st);
-  return mxk::launch_quantize(fmt, in_dtype == MX_BF16, x, nb, codes, scales, aux, st);
+  return mxk::launch_quantize(fmt, in_dtype, x, nb, codes, scales, aux, st);
 }
 
 }  // namespace
@@ -174,7 +174,7 @@ mx_status mx_quantize_batch(mx_format fmt, int block, mx_dtype in_dtype,
   a.wg_start[0] = 0;
   auto flush = [&]() -> hipError_t {
     if (a.n == 0) return hipSuccess;
-    const hipError_t e = mxk::launch_quantize_batch(fmt, in_dtype == MX_BF16, a, hs);
+    const hipError_t e = mxk::launch_quantize_batch(fmt, in_dtype, a, hs);
     a.n = 0;
     a.wg_start[0] = 0;
     return e;
@@ -217,9 +217,9 @@ mx_status mx_dequantize(mx_format fmt, int block, const void* codes, const uint8
   if (forced_launch_failure()) return MX_ERR_DEVICE;
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
-    return from_hip(mxk::launch_exmy(1, exmy_width(fmt), exmy_params(fmt), out_dtype == MX_BF16,
+    return from_hip(mxk::launch_exmy(1, exmy_width(fmt), exmy_params(fmt), out_dtype,
                                      codes, scales, nb, y, nullptr, static_cast<hipStream_t>(stream)));
-  return from_hip(mxk::launch_dequantize(fmt, out_dtype == MX_BF16, codes, scales, aux, nb, y,
+  return from_hip(mxk::launch_dequantize(fmt, out_dtype, codes, scales, aux, nb, y,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -235,9 +235,9 @@ mx_status mx_fake_quantize(mx_format fmt, int block, mx_dtype dtype, const void*
   if (forced_launch_failure()) return MX_ERR_DEVICE;
   const int64_t nb = rows * (cols / MX_BLOCK);
   if (is_exmy(fmt))
-    return from_hip(mxk::launch_exmy(2, exmy_width(fmt), exmy_params(fmt), dtype == MX_BF16, x,
+    return from_hip(mxk::launch_exmy(2, exmy_width(fmt), exmy_params(fmt), dtype, x,
                                      nullptr, nb, y, nullptr, static_cast<hipStream_t>(stream)));
-  return from_hip(mxk::launch_fake_quantize(fmt, dtype == MX_BF16, x, nb, y,
+  return from_hip(mxk::launch_fake_quantize(fmt, dtype, x, nb, y,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -265,7 +265,8 @@ mx_status attention(bool efq, mx_format v_fmt, int block, const void* q, const v
   if (!(v_fmt == MX_FP8_E4M3 || v_fmt == MX_FP6_E2M3 || v_fmt == MX_FP6_E3M2 ||
         v_fmt == MX_FP4_E2M1))
     return MX_ERR_UNSUPPORTED;
-  if (block != MX_BLOCK || d != 128 || !dtype_ok(out_dtype)) return MX_ERR_UNSUPPORTED;
+  if (block != MX_BLOCK || d != 128 || (out_dtype != MX_BF16 && out_dtype != MX_FP32))
+    return MX_ERR_UNSUPPORTED;
   if (heads < 0 || lq < 0 || lk <= 0 || lk % MX_BLOCK != 0) return MX_ERR_SHAPE;
   // int32 indices inside the kernel: every per-head and grid count must fit
   if (heads > INT32_MAX || lq > INT32_MAX - 128 || lk > (1 << 24)) return MX_ERR_SHAPE;

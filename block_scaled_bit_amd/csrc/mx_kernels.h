@@ -25,7 +25,9 @@ struct ExmyParams {
   float dec_sub;
 };
 
-hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
+// dt: the tensor element type, as the C ABI's mx_dtype (0 bf16, 1 fp32,
+// 2 fp16).
+hipError_t launch_quantize(int fmt, int dt, const void* x, int64_t nb, void* codes,
                            uint8_t* scales, uint8_t* aux, hipStream_t st);
 
 // Up to kBatchMax tensors of one MX hardware format (E2M3, E3M2, E2M1,
@@ -42,14 +44,14 @@ struct QuantBatch {
   void* codes[kBatchMax];
   uint8_t* scales[kBatchMax];
 };
-hipError_t launch_quantize_batch(int fmt, bool bf16, const QuantBatch& a, hipStream_t st);
-hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
+hipError_t launch_quantize_batch(int fmt, int dt, const QuantBatch& a, hipStream_t st);
+hipError_t launch_dequantize(int fmt, int dt, const void* codes, const uint8_t* scales,
                              const uint8_t* aux, int64_t nb, void* y, hipStream_t st);
-hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,
+hipError_t launch_fake_quantize(int fmt, int dt, const void* x, int64_t nb, void* y,
                                 hipStream_t st);
 // op 0: quantize (in = x, out = codes, scales_out); op 1: dequantize (in =
 // codes, scales_in, out = y); op 2: fake-quantize (in = x, out = y).
-hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const void* in,
+hipError_t launch_exmy(int op, int width, const ExmyParams& p, int dt, const void* in,
                        const uint8_t* scales_in, int64_t nb, void* out, uint8_t* scales_out,
                        hipStream_t st);
 hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_t cols,

@@ -189,6 +189,57 @@ __device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void
 }
 
 // ---------------------------------------------------------------------------
+// Tensor element types, as the C ABI's mx_dtype.  fp16 tensors (the "Online
+// MXFP6" page, "Start a model": BF16 or FP16 weights) have bf16's 64-byte
+// blocks; their values are widened to fp32 in registers (exactly) and take
+// the fp32 paths, and fp32 results leave rounded once to binary16 (nearest
+// even, overflow to infinity; the canonical fp32 NaN becomes 0x7E00).
+// ---------------------------------------------------------------------------
+constexpr int kBF16 = 0, kF32 = 1, kF16 = 2;
+
+// 16-byte output chunks per block of a tensor of type dt
+constexpr int out_chunks(int dt) { return dt == kF32 ? 8 : 4; }
+
+__device__ __forceinline__ uint32_t f16_to_f32_bits(uint32_t h) {
+  return __float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)h));
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(uint32_t f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(f));
+}
+
+// The 32 values of block b as fp32 patterns, from an fp32 or fp16 tensor.
+template <int DT>
+__device__ __forceinline__ void load_wide(const void* x, int64_t b, uint32_t (&v)[32]) {
+  if constexpr (DT == kF16) {
+    uint32_t d[16];
+    load_bf16_block(x, b, d);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[2 * k] = f16_to_f32_bits(d[k] & 0xFFFFu);
+      v[2 * k + 1] = f16_to_f32_bits(d[k] >> 16);
+    }
+  } else {
+    load_f32_block(x, b, v);
+  }
+}
+
+// A lane's 32 fp32 results stored through the wave's LDS tile into an fp32
+// or fp16 tensor.
+template <int DT>
+__device__ __forceinline__ void store_wide(uint4* __restrict__ lds, void* y, int64_t b0,
+                                           int64_t nb, int lane, const uint32_t (&out)[32]) {
+  if constexpr (DT == kF16) {
+    uint32_t h[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      h[k] = f32_to_f16_bits(out[2 * k]) | (f32_to_f16_bits(out[2 * k + 1]) << 16);
+    store_tile_via_lds<4>(lds, y, b0, nb, lane, h);
+  } else {
+    store_tile_via_lds<8>(lds, y, b0, nb, lane, out);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Coalesced input for a wave tile of 64 bf16 blocks (4 KB): four direct
 // global->LDS loads, each covering 1 KB of consecutive bytes, then lane l
 // reads its block's four 16-byte quarters from LDS.  The quarters of block
@@ -272,12 +323,12 @@ __device__ __forceinline__ void quantize_mx_values(const uint32_t (&d)[N], int64
 }
 
 // bf16 input: one wave tile of 64 blocks per wave (bf16_wave_tile); fp32
-// input: one block per lane.
-template <int F, bool BF16>
+// and fp16 input: one block per lane.
+template <int F, int DT>
 __global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, int64_t nb,
                                                    void* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
-  if constexpr (BF16) {
+  if constexpr (DT == kBF16) {
     __shared__ uint4 lds[4][4 * kTile];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -289,7 +340,7 @@ __global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, i
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
       uint32_t d[32];
-      load_f32_block(x, b, d);
+      load_wide<DT>(x, b, d);
       quantize_mx_values<F>(d, b, codes, scales);
     }
   }
@@ -299,7 +350,7 @@ __global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, i
 // wg_start[i] <= w < wg_start[i + 1] (found from blockIdx and the kernel
 // arguments alone, so i is uniform and its pointers are scalar loads), and
 // its lanes take blocks 256 (w - wg_start[i]) + lane of that tensor.
-template <int F, bool BF16>
+template <int F, int DT>
 __global__ __launch_bounds__(256) void quantize_mx_batch(const QuantBatch a) {
   const uint32_t w = blockIdx.x;
   int i = 0;
@@ -309,24 +360,24 @@ __global__ __launch_bounds__(256) void quantize_mx_batch(const QuantBatch a) {
   // quantize_mx measured no faster on the conversion's layer batches
   const int64_t b = (int64_t)(w - a.wg_start[i]) * 256 + threadIdx.x;
   if (b < a.nb[i]) {
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       uint32_t d[16];
       load_bf16_block(a.x[i], b, d);
       quantize_mx_values<F>(d, b, a.codes[i], a.scales[i]);
     } else {
       uint32_t d[32];
-      load_f32_block(a.x[i], b, d);
+      load_wide<DT>(a.x[i], b, d);
       quantize_mx_values<F>(d, b, a.codes[i], a.scales[i]);
     }
   }
 }
 
-template <int F, bool BF16>
+template <int F, int DT>
 __global__ __launch_bounds__(256) void dequantize_mx(const void* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales,
                                                      int64_t nb, void* __restrict__ y) {
   constexpr int W = Fmt<F>::W;
-  constexpr int NCH = BF16 ? 4 : 8;  // 16-byte output chunks per block
+  constexpr int NCH = out_chunks(DT);  // 16-byte output chunks per block
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -340,36 +391,38 @@ __global__ __launch_bounds__(256) void dequantize_mx(const void* __restrict__ co
     }
     bool fix_nan = (byte == 0xFFu);
     if constexpr (F == F_E4M3) fix_nan |= e4m3_has_nan_code(o);
-    uint32_t d[4 * NCH];
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
+      uint32_t d[16];
       decode_bf16<F>(o, scale_operand(byte), d);
       if (fix_nan) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) d[k] = (byte == 0xFFu) ? kNaN16x2 : canon_nan16x2(d[k]);
       }
+      store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
+      uint32_t d[32];
       decode_f32<F>(o, scale_operand(byte), d);
       if (fix_nan) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) d[k] = (byte == 0xFFu) ? kNaN32 : canon_nan32(d[k]);
       }
+      store_wide<DT>(lds[wave], y, b0, nb, lane, d);
     }
-    store_tile_via_lds<NCH>(lds[wave], y, b0, nb, lane, d);
   }
 }
 
-template <int F, bool BF16>
+template <int F, int DT>
 __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t nb, void* y) {
   constexpr int W = Fmt<F>::W;
-  constexpr int NCH = BF16 ? 4 : 8;
+  constexpr int NCH = out_chunks(DT);
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
     uint32_t o[W];
-    uint32_t d[4 * NCH] = {};
-    if constexpr (BF16) {
+    uint32_t d[DT == kBF16 ? 16 : 32] = {};
+    if constexpr (DT == kBF16) {
       if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
       else if (b < nb) load_bf16_block(x, b, d);
       const uint32_t byte = scale_byte_from_amax<F>(amax_bf16x32(d));
@@ -381,7 +434,7 @@ __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t n
         for (int k = 0; k < 16; ++k) d[k] = kNaN16x2;
       }
     } else {
-      if (b < nb) load_f32_block(x, b, d);
+      if (b < nb) load_wide<DT>(x, b, d);
       const uint32_t byte = scale_byte_from_amax<F>(amax_f32x32(d));
       const float sc = scale_operand(byte);
       encode_f32<F>(d, sc, o);
@@ -393,7 +446,8 @@ __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t n
     }
     // every lane has read its block before any lane of the wave stores, so
     // y == x is safe
-    store_tile_via_lds<NCH>(lds[wave], y, b0, nb, lane, d);
+    if constexpr (DT == kBF16) store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
+    else store_wide<DT>(lds[wave], y, b0, nb, lane, d);
   }
 }
 
@@ -408,9 +462,9 @@ __device__ __forceinline__ uint32_t axs6_block_byte(const uint32_t (&v)[32]) {
   return scale_byte_from_amax<F_AXS6>(amax);
 }
 
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ void load_values(const void* x, int64_t b, uint32_t (&v)[32]) {
-  if constexpr (BF16) {
+  if constexpr (DT == kBF16) {
     uint32_t d[16];
     load_bf16_block(x, b, d);
 #pragma unroll
@@ -419,7 +473,7 @@ __device__ __forceinline__ void load_values(const void* x, int64_t b, uint32_t (
       v[2 * k + 1] = d[k] & 0xFFFF0000u;
     }
   } else {
-    load_f32_block(x, b, v);
+    load_wide<DT>(x, b, v);
   }
 }
 
@@ -449,7 +503,7 @@ __device__ __forceinline__ void quantize_axs6_values(const uint32_t (&v)[32], ui
   if ((b & 3) == 0) aux[b >> 2] = 0;
 }
 
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x, int64_t nb,
                                                      void* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
@@ -460,7 +514,7 @@ __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x,
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     uint32_t v[32];
     uint32_t byte;
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       uint32_t d[16];
       load_bf16_block(x, b, d);
       byte = scale_byte_from_amax<F_AXS6>(amax_bf16x32(d));
@@ -470,16 +524,16 @@ __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x,
         v[2 * k + 1] = d[k] & 0xFFFF0000u;
       }
     } else {
-      load_values<BF16>(x, b, v);
+      load_values<DT>(x, b, v);
       byte = axs6_block_byte(v);
     }
     quantize_axs6_values(v, byte, b, codes, scales, aux);
   }
 }
 
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t nb, void* y) {
-  constexpr int NCH = BF16 ? 4 : 8;
+  constexpr int NCH = out_chunks(DT);
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -487,7 +541,7 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
     const int64_t b0 = t * kTile, b = b0 + lane;
     uint32_t v[32] = {};
     uint32_t byte;
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       uint32_t d[16] = {};
       if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
       else if (b < nb) load_bf16_block(x, b, d);
@@ -498,7 +552,7 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
         v[2 * k + 1] = d[k] & 0xFFFF0000u;
       }
     } else {
-      if (b < nb) load_values<BF16>(x, b, v);
+      if (b < nb) load_values<DT>(x, b, v);
       byte = axs6_block_byte(v);
     }
     // the same rounding as quantize_axs6, on signed values: 16 |v| / X =
@@ -516,7 +570,7 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
       out[k] = __float_as_uint(__builtin_ldexpf(m, e_out));
     }
     const bool poisoned = byte == 0xFFu;  // a block with a NaN or an infinity
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       // every result is a bf16 value: keep the top halves
       uint32_t d[16];
 #pragma unroll
@@ -526,17 +580,17 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
     } else {
 #pragma unroll
       for (int k = 0; k < 32; ++k) out[k] = poisoned ? kNaN32 : out[k];
-      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+      store_wide<DT>(lds[wave], y, b0, nb, lane, out);
     }
   }
 }
 
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const uint8_t* __restrict__ aux, int64_t nb,
                                                        void* __restrict__ y) {
-  constexpr int NCH = BF16 ? 4 : 8;
+  constexpr int NCH = out_chunks(DT);
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -558,7 +612,7 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
       const float val = decode_mag<F_AXS6>(code & 31u, sexp);
       out[k] = poisoned ? kNaN32 : (__float_as_uint(val) | ((code >> 5) << 31));
     }
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       uint32_t d[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k)
@@ -566,7 +620,7 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
                (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
       store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
-      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+      store_wide<DT>(lds[wave], y, b0, nb, lane, out);
     }
   }
 }
@@ -682,7 +736,7 @@ __device__ __forceinline__ float exmy_value(uint32_t mag, int scale_exp, const E
   return exmy_decode(mag, scale_exp, p);
 }
 
-template <int W, bool BF16, bool M0>
+template <int W, int DT, bool M0>
 __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x, int64_t nb,
                                                      uint32_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales, ExmyParams p) {
@@ -699,7 +753,7 @@ __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     uint32_t v[32];
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       uint32_t d[16];
       load_bf16_block(x, b, d);
 #pragma unroll
@@ -709,23 +763,23 @@ __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x,
       }
       block(b, v, exmy_byte_from_amax(amax_bf16x32(d), p));
     } else {
-      load_f32_block(x, b, v);
+      load_wide<DT>(x, b, v);
       block(b, v, exmy_byte_from_amax(amax_f32x32(v), p));
     }
   }
 }
 
-template <int W, bool BF16, bool M0>
+template <int W, int DT, bool M0>
 __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t nb, void* y,
                                                           ExmyParams p) {
-  constexpr int NCH = BF16 ? 4 : 8;
+  constexpr int NCH = out_chunks(DT);
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves) {
     const int64_t b0 = t * kTile, b = b0 + lane;
     uint32_t v[32] = {}, c[32], out[32];
-    if (b < nb) load_values<BF16>(x, b, v);
+    if (b < nb) load_values<DT>(x, b, v);
     const uint32_t byte = exmy_block_byte(v, p);
     exmy_codes<W, M0>(v, byte, p, c);
     const int sexp = (int)byte - 127;
@@ -734,7 +788,7 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
       const float val = exmy_value<W == 9 && M0>(c[k] & ((1u << (W - 1)) - 1u), sexp, p);
       out[k] = (byte == 0xFFu) ? kNaN32 : (__float_as_uint(val) | (v[k] & 0x80000000u));
     }
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       // the results are bf16 values: round to nearest even (exact unless a
       // subnormal product needs it)
       uint32_t d[16];
@@ -744,17 +798,17 @@ __global__ __launch_bounds__(256) void fake_quantize_exmy(const void* x, int64_t
                (f32_to_bf16_rne(__uint_as_float(out[2 * k + 1])) << 16);
       store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
-      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+      store_wide<DT>(lds[wave], y, b0, nb, lane, out);
     }
   }
 }
 
-template <int W, bool BF16, bool E8>
+template <int W, int DT, bool E8>
 __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        int64_t nb, void* __restrict__ y,
                                                        ExmyParams p) {
-  constexpr int NCH = BF16 ? 4 : 8;
+  constexpr int NCH = out_chunks(DT);
   __shared__ uint4 lds[4][tile_slots(NCH)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
@@ -779,7 +833,7 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
 #pragma unroll
       for (int k = 0; k < 32; ++k) out[k] = kNaN32;
     }
-    if constexpr (BF16) {
+    if constexpr (DT == kBF16) {
       // every eXmY value has at most 8 significant bits, so it is a bf16
       // value whenever it is an fp32 normal (or zero, inf, NaN): the top
       // half of the bit pattern, no rounding.  Only blocks whose smallest
@@ -796,7 +850,7 @@ __global__ __launch_bounds__(256) void dequantize_exmy(const uint32_t* __restric
       }
       store_tile_via_lds<4>(lds[wave], y, b0, nb, lane, d);
     } else {
-      store_tile_via_lds<8>(lds[wave], y, b0, nb, lane, out);
+      store_wide<DT>(lds[wave], y, b0, nb, lane, out);
     }
   }
 }
@@ -1018,58 +1072,57 @@ static inline dim3 grid_for(int64_t work, int per_wg) {
     default: return hipErrorInvalidValue;                          \
   }
 
-hipError_t launch_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* codes,
+#define MXK_SWITCH_DT(dt, BODY)                                  \
+  switch (dt) {                                                  \
+    case kBF16: { constexpr int DD = kBF16; BODY; } break;       \
+    case kF32: { constexpr int DD = kF32; BODY; } break;         \
+    case kF16: { constexpr int DD = kF16; BODY; } break;         \
+    default: return hipErrorInvalidValue;                        \
+  }
+
+hipError_t launch_quantize(int fmt, int dt, const void* x, int64_t nb, void* codes,
                            uint8_t* scales, uint8_t* aux, hipStream_t st) {
   const dim3 grid = grid_for(nb, 256), block(256);
   if (fmt == F_AXS6) {
-    if (bf16) hipLaunchKernelGGL(quantize_axs6<true>, grid, block, 0, st, x, nb, codes, scales, aux);
-    else hipLaunchKernelGGL(quantize_axs6<false>, grid, block, 0, st, x, nb, codes, scales, aux);
+    MXK_SWITCH_DT(dt, hipLaunchKernelGGL(quantize_axs6<DD>, grid, block, 0, st, x, nb, codes,
+                                         scales, aux));
     return hipGetLastError();
   }
-  MXK_SWITCH_MX(fmt, {
-    if (bf16) hipLaunchKernelGGL((quantize_mx<FF, true>), grid, block, 0, st, x, nb, codes, scales);
-    else hipLaunchKernelGGL((quantize_mx<FF, false>), grid, block, 0, st, x, nb, codes, scales);
-  });
+  MXK_SWITCH_MX(fmt, MXK_SWITCH_DT(dt, hipLaunchKernelGGL((quantize_mx<FF, DD>), grid, block, 0,
+                                                           st, x, nb, codes, scales)));
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_batch(int fmt, bool bf16, const QuantBatch& a, hipStream_t st) {
+hipError_t launch_quantize_batch(int fmt, int dt, const QuantBatch& a, hipStream_t st) {
   if (a.n < 1 || a.n > kBatchMax) return hipErrorInvalidValue;
   const dim3 grid(a.wg_start[a.n]), block(256);
-  MXK_SWITCH_MX(fmt, {
-    if (bf16) hipLaunchKernelGGL((quantize_mx_batch<FF, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((quantize_mx_batch<FF, false>), grid, block, 0, st, a);
-  });
+  MXK_SWITCH_MX(fmt, MXK_SWITCH_DT(dt, hipLaunchKernelGGL((quantize_mx_batch<FF, DD>), grid,
+                                                           block, 0, st, a)));
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(int fmt, bool bf16, const void* codes, const uint8_t* scales,
+hipError_t launch_dequantize(int fmt, int dt, const void* codes, const uint8_t* scales,
                              const uint8_t* aux, int64_t nb, void* y, hipStream_t st) {
   const dim3 grid = grid_for(nb, 4 * kTile), block(256);  // one 64-block tile per wave
   if (fmt == F_AXS6) {
-    if (bf16) hipLaunchKernelGGL(dequantize_axs6<true>, grid, block, 0, st, codes, scales, aux, nb, y);
-    else hipLaunchKernelGGL(dequantize_axs6<false>, grid, block, 0, st, codes, scales, aux, nb, y);
+    MXK_SWITCH_DT(dt, hipLaunchKernelGGL(dequantize_axs6<DD>, grid, block, 0, st, codes, scales,
+                                         aux, nb, y));
     return hipGetLastError();
   }
-  MXK_SWITCH_MX(fmt, {
-    if (bf16) hipLaunchKernelGGL((dequantize_mx<FF, true>), grid, block, 0, st, codes, scales, nb, y);
-    else hipLaunchKernelGGL((dequantize_mx<FF, false>), grid, block, 0, st, codes, scales, nb, y);
-  });
+  MXK_SWITCH_MX(fmt, MXK_SWITCH_DT(dt, hipLaunchKernelGGL((dequantize_mx<FF, DD>), grid, block, 0,
+                                                           st, codes, scales, nb, y)));
   return hipGetLastError();
 }
 
-hipError_t launch_fake_quantize(int fmt, bool bf16, const void* x, int64_t nb, void* y,
+hipError_t launch_fake_quantize(int fmt, int dt, const void* x, int64_t nb, void* y,
                                 hipStream_t st) {
   const dim3 grid = grid_for(nb, 4 * kTile), block(256);  // one 64-block tile per wave
   if (fmt == F_AXS6) {
-    if (bf16) hipLaunchKernelGGL(fake_quantize_axs6<true>, grid, block, 0, st, x, nb, y);
-    else hipLaunchKernelGGL(fake_quantize_axs6<false>, grid, block, 0, st, x, nb, y);
+    MXK_SWITCH_DT(dt, hipLaunchKernelGGL(fake_quantize_axs6<DD>, grid, block, 0, st, x, nb, y));
     return hipGetLastError();
   }
-  MXK_SWITCH_MX(fmt, {
-    if (bf16) hipLaunchKernelGGL((fake_quantize_mx<FF, true>), grid, block, 0, st, x, nb, y);
-    else hipLaunchKernelGGL((fake_quantize_mx<FF, false>), grid, block, 0, st, x, nb, y);
-  });
+  MXK_SWITCH_MX(fmt, MXK_SWITCH_DT(dt, hipLaunchKernelGGL((fake_quantize_mx<FF, DD>), grid, block,
+                                                           0, st, x, nb, y)));
   return hipGetLastError();
 }
 
@@ -1132,38 +1185,24 @@ hipError_t launch_softmax_quantize(int fmt, const float* s, int64_t rows, int64_
     default: return hipErrorInvalidValue;                   \
   }
 
-hipError_t launch_exmy(int op, int width, const ExmyParams& p, bool bf16, const void* in,
+hipError_t launch_exmy(int op, int width, const ExmyParams& p, int dt, const void* in,
                        const uint8_t* scales_in, int64_t nb, void* out, uint8_t* scales_out,
                        hipStream_t st) {
   const dim3 block(256);
   const dim3 grid = (op == 0) ? grid_for(nb, 256) : grid_for(nb, 4 * kTile);
   // exponent-only formats (m = 0) need the even-exponent tie rule; width 9
   // with m = 0 is e8m0, which has code paths of its own
-#define MXK_EXMY_LAUNCH(M0)                                                                     \
-  MXK_SWITCH_WIDTH(width, {                                                                     \
-    if (op == 0) {                                                                              \
-      if (bf16)                                                                                 \
-        hipLaunchKernelGGL((quantize_exmy<WW, true, M0>), grid, block, 0, st, in, nb,           \
-                           (uint32_t*)out, scales_out, p);                                      \
-      else                                                                                      \
-        hipLaunchKernelGGL((quantize_exmy<WW, false, M0>), grid, block, 0, st, in, nb,          \
-                           (uint32_t*)out, scales_out, p);                                      \
-    } else if (op == 1) {                                                                       \
-      if (bf16)                                                                                 \
-        hipLaunchKernelGGL((dequantize_exmy<WW, true, M0 && WW == 9>), grid, block, 0, st,      \
-                           (const uint32_t*)in, scales_in, nb, out, p);                         \
-      else                                                                                      \
-        hipLaunchKernelGGL((dequantize_exmy<WW, false, M0 && WW == 9>), grid, block, 0, st,     \
-                           (const uint32_t*)in, scales_in, nb, out, p);                         \
-    } else {                                                                                    \
-      if (bf16)                                                                                 \
-        hipLaunchKernelGGL((fake_quantize_exmy<WW, true, M0>), grid, block, 0, st, in, nb, out, \
-                           p);                                                                  \
-      else                                                                                      \
-        hipLaunchKernelGGL((fake_quantize_exmy<WW, false, M0>), grid, block, 0, st, in, nb,     \
-                           out, p);                                                             \
-    }                                                                                           \
-  })
+#define MXK_EXMY_LAUNCH(M0)                                                                    \
+  MXK_SWITCH_WIDTH(width, MXK_SWITCH_DT(dt, {                                                  \
+    if (op == 0)                                                                               \
+      hipLaunchKernelGGL((quantize_exmy<WW, DD, M0>), grid, block, 0, st, in, nb,              \
+                         (uint32_t*)out, scales_out, p);                                       \
+    else if (op == 1)                                                                          \
+      hipLaunchKernelGGL((dequantize_exmy<WW, DD, M0 && WW == 9>), grid, block, 0, st,         \
+                         (const uint32_t*)in, scales_in, nb, out, p);                          \
+    else                                                                                       \
+      hipLaunchKernelGGL((fake_quantize_exmy<WW, DD, M0>), grid, block, 0, st, in, nb, out, p); \
+  }))
   if (p.m == 0) {
     MXK_EXMY_LAUNCH(true);
   } else {

@@ -38,11 +38,11 @@
  *   dequantize  sign * value(code) * X, rounded to the output type
  *               (nearest-even); 0xFF blocks, E4M3 NaN codes and AXS-6
  *               blocks whose config is not 0 give the canonical quiet NaN
- *               (bf16 0x7FC0, fp32 0x7FC00000).
+ *               (bf16 0x7FC0, fp32 0x7FC00000, fp16 0x7E00).
  *
  * Buffers (caller-owned device memory, contiguous, row-major; nb = rows *
  * cols / 32 blocks, block b = row * (cols/32) + j):
- *   x, y     [rows, cols] bf16 or fp32, 16-byte aligned
+ *   x, y     [rows, cols] bf16, fp32 or fp16 (mx_dtype), 16-byte aligned
  *   codes    [rows, cols/32, bpb] bytes, bpb = 24 (FP6, AXS-6), 16 (FP4),
  *            32 (FP8), 4w (eXmY of width w); 16-byte aligned
  *   scales   [rows, cols/32] bytes (E8M0; AXS-6 shared exponent, same
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 6
+#define MX_ABI_VERSION 7
 #define MX_BLOCK 32
 
 typedef enum {
@@ -96,7 +96,13 @@ typedef enum {
  * accepted by mx_softmax_quantize. */
 #define MX_EXMY(e, m) ((mx_format)(0x100 | ((e) << 4) | (m)))
 
-typedef enum { MX_BF16 = 0, MX_FP32 = 1 } mx_dtype;
+/* Tensor element types.  mx_quantize, mx_quantize_batch, mx_dequantize and
+ * mx_fake_quantize take all three ("Online MXFP6", "Start a model": BF16 or
+ * FP16 weights; fp16 from ABI version 7): fp16 values are read exactly and
+ * results are rounded once to binary16 (nearest even, overflow to
+ * infinity, NaN as 0x7E00).  mx_softmax_quantize reads fp32 scores; the
+ * attention forward writes bf16 or fp32. */
+typedef enum { MX_BF16 = 0, MX_FP32 = 1, MX_FP16 = 2 } mx_dtype;
 
 typedef enum {
   MX_OK = 0,

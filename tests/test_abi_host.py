@@ -51,7 +51,7 @@ def test_library_is_gfx950_only(mx):
 
 
 def test_version_and_status_strings(mx):
-    assert mx.mx_abi_version() == 6
+    assert mx.mx_abi_version() == 7
     for s in range(0, 8):
         assert isinstance(mx.mx_status_str(s), str) and mx.mx_status_str(s)
 
@@ -76,7 +76,8 @@ A = 0x10000  # a 16-byte aligned fake device address (never dereferenced)
     ((0, 32, 0, A, -1, 32, A, A, None), SHAPE),       # negative rows
     ((0, 16, 0, A, 4, 32, A, A, None), UNSUP),        # block size
     ((5, 32, 0, A, 4, 32, A, A, None), UNSUP),        # format
-    ((0, 32, 2, A, 4, 32, A, A, None), UNSUP),        # dtype
+    ((0, 32, 3, A, 4, 32, A, A, None), UNSUP),        # dtype
+    ((0, 32, 2, None, 4, 32, A, A, None), NULL),      # fp16 is accepted
     ((0, 32, 0, None, 4, 32, A, A, None), NULL),      # x
     ((0, 32, 0, A, 4, 32, None, A, None), NULL),      # codes
     ((0, 32, 0, A, 4, 32, A, None, None), NULL),      # scales
@@ -224,6 +225,7 @@ def test_attention_argument_errors(mx):
     assert call(block=16) == UNSUP
     assert call(d=64) == UNSUP
     assert call(out=7) == UNSUP
+    assert call(out=mx.MX_FP16) == UNSUP  # bf16 or fp32 output only
     assert call(lk=0) == SHAPE
     assert call(lk=48) == SHAPE
     assert call(lk=(1 << 24) + 32) == SHAPE
