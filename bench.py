@@ -439,6 +439,37 @@ def secondary(mx, steps, threads, check=True):
         del cs
     del xs, ys, ss, w
 
+    # -- the same weight as fp16 ("Online MXFP6", "Start a model": BF16 or
+    #    FP16 weights): E2M3 quantize, and dequantize back to fp16
+    w = workloads.linear_weight_f16()
+    rows, cols = w.shape
+    nb = rows * cols // 32
+    note = "linear_weight_f16 fp16 14336x4096"
+    n = rotation_sets(rows * cols * 4 + nb * 25)
+    xs = [torch.from_numpy(w).cuda() for _ in range(n)]
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
+    ss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    cs = [torch.empty(nb * 24, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    F16 = mx.MX_FP16
+    q = lambda i: mx.mx_quantize(0, 32, F16, xs[i], rows, cols, cs[i], ss[i], None, st)
+    dq = lambda i: mx.mx_dequantize(0, 32, cs[i], ss[i], None, rows, cols, F16, ys[i], st)
+    S.time("quantize_e2m3_fp16", q, n, rows * cols * 2, nb * 25, note, copy_bpb=(64, 25))
+    S.launch("q16", q)(0)
+    S.time("dequantize_e2m3_to_fp16", dq, n, nb * 25, rows * cols * 2, note, copy_bpb=(25, 64))
+    S.launch("dq16", dq)(0)
+    torch.cuda.synchronize()
+    if check:
+        gc, gs, gy = host(cs[0]), host(ss[0]), host(ys[0])
+        (oc, os_, _), t_q = S.oracle(lambda a, b: oracle.quantize(0, w[a:b]), rows)
+        oy, t_dq = S.oracle(lambda a, b: oracle.dequantize(
+            0, oc[a:b], os_[a:b], None, b - a, cols, oracle.F16), rows)
+        S.parity("quantize_e2m3_fp16", [(gc, oc), (gs, os_)], rows * cols * 2, t_q,
+                 "all 14336 rows: codes, scales")
+        S.parity("dequantize_e2m3_to_fp16", [(gy, oy)], nb * 25, t_dq,
+                 "all 14336 rows: fp16 output")
+        del oc, os_, oy, gc, gs, gy
+    del xs, ys, ss, cs, w
+
     # -- AXS-6 weight: fake-quantize and quantize (+ config plane); bits per
     #    value and each block's largest error
     a = workloads.axs6_weight()

@@ -28,6 +28,8 @@ typedef float f32x32_t __attribute__((ext_vector_type(32)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x32_t __attribute__((ext_vector_type(32)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float scale_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
 
@@ -41,6 +43,18 @@ __device__ __forceinline__ uint32_t amax_bf16x32(const uint32_t (&d)[16]) {
     m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, d[k] & 0x7FFF7FFFu));
   const uint32_t lo = m[0], hi = m[1];
   return (hi > lo ? hi : lo) << 16;
+}
+
+// The same for 32 fp16: finite fp16 magnitudes also order as their bit
+// patterns, with inf and NaN above them; the result is widened exactly to
+// an fp32 pattern (inf and NaN stay non-finite).
+__device__ __forceinline__ uint32_t amax_f16x32(const uint32_t (&d)[16]) {
+  u16x2_t m = {0, 0};
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, d[k] & 0x7FFF7FFFu));
+  const uint16_t h = m[1] > m[0] ? m[1] : m[0];
+  return __float_as_uint((float)__builtin_bit_cast(_Float16, h));
 }
 
 __device__ __forceinline__ uint32_t amax_f32x32(const uint32_t (&d)[32]) {
@@ -91,6 +105,42 @@ __device__ __forceinline__ void encode_bf16(const uint32_t (&d)[16], float sc, u
       s16x2_t w = {0, 0};
       w = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w, __builtin_bit_cast(bf16x2_t, d[2 * j]), sc, false);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w, __builtin_bit_cast(bf16x2_t, d[2 * j + 1]), sc, true);
+      o[j] = e4m3_saturate4(__builtin_bit_cast(uint32_t, w));
+    }
+  }
+}
+
+// The same from 32 fp16 held as 16 dwords (element 2k in the low half of
+// dword k), with the fp16-source forms of the instructions.
+template <int F>
+__device__ __forceinline__ void encode_f16(const uint32_t (&d)[16], float sc, uint32_t (&o)[Fmt<F>::W]) {
+  if constexpr (F == F_E2M3 || F == F_E3M2) {
+    u32x16_t u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) u[k] = d[k];
+    const f16x32_t v = __builtin_bit_cast(f16x32_t, u);
+    u32x6_t r;
+    if constexpr (F == F_E2M3) r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(v, sc);
+    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf6_f16(v, sc);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) o[k] = r[k];
+  } else if constexpr (F == F_E2M1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(w, __builtin_bit_cast(f16x2_t, d[4 * j + 0]), sc, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(w, __builtin_bit_cast(f16x2_t, d[4 * j + 1]), sc, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(w, __builtin_bit_cast(f16x2_t, d[4 * j + 2]), sc, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(w, __builtin_bit_cast(f16x2_t, d[4 * j + 3]), sc, 3);
+      o[j] = w;
+    }
+  } else {
+    static_assert(F == F_E4M3, "hardware encode covers the MX formats");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s16x2_t w = {0, 0};
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, __builtin_bit_cast(f16x2_t, d[2 * j]), sc, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, __builtin_bit_cast(f16x2_t, d[2 * j + 1]), sc, true);
       o[j] = e4m3_saturate4(__builtin_bit_cast(uint32_t, w));
     }
   }

@@ -31,10 +31,10 @@ constexpr uint32_t kNaN32 = 0x7FC00000u;
 constexpr uint32_t kNaN16x2 = 0x7FC07FC0u;
 
 // ---------------------------------------------------------------------------
-// Memory helpers: block b of bf16 is 4 x 16 B at b*64, of fp32 8 x 16 B at
-// b*128; packed codes are W dwords at b*4W.
+// Memory helpers: block b of a 16-bit tensor (bf16 or fp16) is 4 x 16 B at
+// b*64, of fp32 8 x 16 B at b*128; packed codes are W dwords at b*4W.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load_bf16_block(const void* x, int64_t b, uint32_t (&d)[16]) {
+__device__ __forceinline__ void load_block16(const void* x, int64_t b, uint32_t (&d)[16]) {
   const uint4* p = reinterpret_cast<const uint4*>(x) + b * 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -207,17 +207,23 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(uint32_t f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(f));
 }
 
+// 32 fp16 values (16 dwords, element 2k in the low half of dword k) as
+// fp32 patterns; exact.
+__device__ __forceinline__ void widen_f16(const uint32_t (&d)[16], uint32_t (&v)[32]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    v[2 * k] = f16_to_f32_bits(d[k] & 0xFFFFu);
+    v[2 * k + 1] = f16_to_f32_bits(d[k] >> 16);
+  }
+}
+
 // The 32 values of block b as fp32 patterns, from an fp32 or fp16 tensor.
 template <int DT>
 __device__ __forceinline__ void load_wide(const void* x, int64_t b, uint32_t (&v)[32]) {
   if constexpr (DT == kF16) {
     uint32_t d[16];
-    load_bf16_block(x, b, d);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      v[2 * k] = f16_to_f32_bits(d[k] & 0xFFFFu);
-      v[2 * k + 1] = f16_to_f32_bits(d[k] >> 16);
-    }
+    load_block16(x, b, d);
+    widen_f16(d, v);
   } else {
     load_f32_block(x, b, v);
   }
@@ -240,7 +246,8 @@ __device__ __forceinline__ void store_wide(uint4* __restrict__ lds, void* y, int
 }
 
 // ---------------------------------------------------------------------------
-// Coalesced input for a wave tile of 64 bf16 blocks (4 KB): four direct
+// Coalesced input for a wave tile of 64 blocks of 16-bit values (4 KB of
+// bf16 or fp16): four direct
 // global->LDS loads, each covering 1 KB of consecutive bytes, then lane l
 // reads its block's four 16-byte quarters from LDS.  The quarters of block
 // b sit at slots 4b + (q ^ ((b / 4) % 4)): the 16 lanes of one LDS read
@@ -255,7 +262,7 @@ typedef __attribute__((address_space(1))) const void glob_void_t;
 
 __device__ __forceinline__ int quarter_slot(int b, int q) { return 4 * b + (q ^ ((b >> 2) & 3)); }
 
-__device__ __forceinline__ void load_bf16_tile_coalesced(const void* x, int64_t b0, uint4* tile,
+__device__ __forceinline__ void load_tile16_coalesced(const void* x, int64_t b0, uint4* tile,
                                                          int lane, uint32_t (&d)[16]) {
   const uint4* src = reinterpret_cast<const uint4*>(x) + 4 * b0;
 #pragma unroll
@@ -280,36 +287,39 @@ __device__ __forceinline__ void load_bf16_tile_coalesced(const void* x, int64_t 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Wave tile t of a bf16 tensor of nb blocks: lane l gets block 64 t + l,
+// Wave tile t of a 16-bit tensor of nb blocks: lane l gets block 64 t + l,
 // read through LDS in 1 KB instructions when the tile is whole (the MX
 // quantizer reads its input this way 1.5-3.4 % faster than with four
 // 16-byte loads per lane), else directly; fn(b, d) runs for each block
 // b < nb.  t is the same for the whole wave.
 template <typename Fn>
-__device__ __forceinline__ void bf16_wave_tile(const void* x, int64_t t, int64_t nb, uint4* tile,
+__device__ __forceinline__ void wave_tile16(const void* x, int64_t t, int64_t nb, uint4* tile,
                                                int lane, Fn&& fn) {
   const int64_t b0 = t * kTile, b = b0 + lane;
   uint32_t d[16] = {};
-  if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, tile, lane, d);
-  else if (b < nb) load_bf16_block(x, b, d);
+  if (b0 + kTile <= nb) load_tile16_coalesced(x, b0, tile, lane, d);
+  else if (b < nb) load_block16(x, b, d);
   if (b < nb) fn(b, d);
 }
 
 // ---------------------------------------------------------------------------
 // MX formats (E2M3, E3M2, E2M1, E4M3): hardware conversions
 // ---------------------------------------------------------------------------
-// Block b of one tensor from its values (16 dwords of bf16 pairs or 32 fp32
-// patterns): scale byte, codes, and both stores.
-template <int F, int N>
-__device__ __forceinline__ void quantize_mx_values(const uint32_t (&d)[N], int64_t b,
-                                                   void* __restrict__ codes,
+// Block b of one tensor from its values of type DT (16 dwords of bf16 or
+// fp16 pairs, or 32 fp32 patterns): scale byte, codes, and both stores.
+template <int F, int DT>
+__device__ __forceinline__ void quantize_mx_values(const uint32_t (&d)[DT == kF32 ? 32 : 16],
+                                                   int64_t b, void* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
   constexpr int W = Fmt<F>::W;
   uint32_t o[W];
   uint32_t byte;
-  if constexpr (N == 16) {
+  if constexpr (DT == kBF16) {
     byte = scale_byte_from_amax<F>(amax_bf16x32(d));
     encode_bf16<F>(d, scale_operand(byte), o);
+  } else if constexpr (DT == kF16) {
+    byte = scale_byte_from_amax<F>(amax_f16x32(d));
+    encode_f16<F>(d, scale_operand(byte), o);
   } else {
     byte = scale_byte_from_amax<F>(amax_f32x32(d));
     encode_f32<F>(d, scale_operand(byte), o);
@@ -322,26 +332,26 @@ __device__ __forceinline__ void quantize_mx_values(const uint32_t (&d)[N], int64
   scales[b] = (uint8_t)byte;
 }
 
-// bf16 input: one wave tile of 64 blocks per wave (bf16_wave_tile); fp32
-// and fp16 input: one block per lane.
+// bf16 and fp16 input: one wave tile of 64 blocks per wave (wave_tile16);
+// fp32 input: one block per lane.
 template <int F, int DT>
 __global__ __launch_bounds__(256) void quantize_mx(const void* __restrict__ x, int64_t nb,
                                                    void* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT != kF32) {
     __shared__ uint4 lds[4][4 * kTile];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves)
-      bf16_wave_tile(x, t, nb, lds[wave], lane, [&](int64_t b, const uint32_t (&d)[16]) {
-        quantize_mx_values<F>(d, b, codes, scales);
+      wave_tile16(x, t, nb, lds[wave], lane, [&](int64_t b, const uint32_t (&d)[16]) {
+        quantize_mx_values<F, DT>(d, b, codes, scales);
       });
   } else {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
       uint32_t d[32];
       load_wide<DT>(x, b, d);
-      quantize_mx_values<F>(d, b, codes, scales);
+      quantize_mx_values<F, DT>(d, b, codes, scales);
     }
   }
 }
@@ -360,14 +370,14 @@ __global__ __launch_bounds__(256) void quantize_mx_batch(const QuantBatch a) {
   // quantize_mx measured no faster on the conversion's layer batches
   const int64_t b = (int64_t)(w - a.wg_start[i]) * 256 + threadIdx.x;
   if (b < a.nb[i]) {
-    if constexpr (DT == kBF16) {
+    if constexpr (DT != kF32) {
       uint32_t d[16];
-      load_bf16_block(a.x[i], b, d);
-      quantize_mx_values<F>(d, b, a.codes[i], a.scales[i]);
+      load_block16(a.x[i], b, d);
+      quantize_mx_values<F, DT>(d, b, a.codes[i], a.scales[i]);
     } else {
       uint32_t d[32];
       load_wide<DT>(a.x[i], b, d);
-      quantize_mx_values<F>(d, b, a.codes[i], a.scales[i]);
+      quantize_mx_values<F, DT>(d, b, a.codes[i], a.scales[i]);
     }
   }
 }
@@ -423,8 +433,8 @@ __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t n
     uint32_t o[W];
     uint32_t d[DT == kBF16 ? 16 : 32] = {};
     if constexpr (DT == kBF16) {
-      if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
-      else if (b < nb) load_bf16_block(x, b, d);
+      if (b0 + kTile <= nb) load_tile16_coalesced(x, b0, lds[wave], lane, d);  // whole tile
+      else if (b < nb) load_block16(x, b, d);
       const uint32_t byte = scale_byte_from_amax<F>(amax_bf16x32(d));
       const float sc = scale_operand(byte);
       encode_bf16<F>(d, sc, o);
@@ -434,10 +444,19 @@ __global__ __launch_bounds__(256) void fake_quantize_mx(const void* x, int64_t n
         for (int k = 0; k < 16; ++k) d[k] = kNaN16x2;
       }
     } else {
-      if (b < nb) load_wide<DT>(x, b, d);
-      const uint32_t byte = scale_byte_from_amax<F>(amax_f32x32(d));
+      uint32_t byte;
+      if constexpr (DT == kF16) {  // encoded from the fp16 values, decoded to fp32
+        uint32_t h[16] = {};
+        if (b0 + kTile <= nb) load_tile16_coalesced(x, b0, lds[wave], lane, h);  // whole tile
+        else if (b < nb) load_block16(x, b, h);
+        byte = scale_byte_from_amax<F>(amax_f16x32(h));
+        encode_f16<F>(h, scale_operand(byte), o);
+      } else {
+        if (b < nb) load_wide<DT>(x, b, d);
+        byte = scale_byte_from_amax<F>(amax_f32x32(d));
+        encode_f32<F>(d, scale_operand(byte), o);
+      }
       const float sc = scale_operand(byte);
-      encode_f32<F>(d, sc, o);
       decode_f32<F>(o, sc, d);
       if (byte == 0xFFu) {
 #pragma unroll
@@ -466,7 +485,7 @@ template <int DT>
 __device__ __forceinline__ void load_values(const void* x, int64_t b, uint32_t (&v)[32]) {
   if constexpr (DT == kBF16) {
     uint32_t d[16];
-    load_bf16_block(x, b, d);
+    load_block16(x, b, d);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       v[2 * k] = d[k] << 16;
@@ -516,7 +535,7 @@ __global__ __launch_bounds__(256) void quantize_axs6(const void* __restrict__ x,
     uint32_t byte;
     if constexpr (DT == kBF16) {
       uint32_t d[16];
-      load_bf16_block(x, b, d);
+      load_block16(x, b, d);
       byte = scale_byte_from_amax<F_AXS6>(amax_bf16x32(d));
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -543,8 +562,8 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
     uint32_t byte;
     if constexpr (DT == kBF16) {
       uint32_t d[16] = {};
-      if (b0 + kTile <= nb) load_bf16_tile_coalesced(x, b0, lds[wave], lane, d);  // whole tile
-      else if (b < nb) load_bf16_block(x, b, d);
+      if (b0 + kTile <= nb) load_tile16_coalesced(x, b0, lds[wave], lane, d);  // whole tile
+      else if (b < nb) load_block16(x, b, d);
       byte = scale_byte_from_amax<F_AXS6>(amax_bf16x32(d));
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -552,7 +571,14 @@ __global__ __launch_bounds__(256) void fake_quantize_axs6(const void* x, int64_t
         v[2 * k + 1] = d[k] & 0xFFFF0000u;
       }
     } else {
-      if (b < nb) load_values<DT>(x, b, v);
+      if constexpr (DT == kF16) {
+        uint32_t h[16] = {};
+        if (b0 + kTile <= nb) load_tile16_coalesced(x, b0, lds[wave], lane, h);  // whole tile
+        else if (b < nb) load_block16(x, b, h);
+        widen_f16(h, v);
+      } else if (b < nb) {
+        load_values<DT>(x, b, v);
+      }
       byte = axs6_block_byte(v);
     }
     // the same rounding as quantize_axs6, on signed values: 16 |v| / X =
@@ -755,7 +781,7 @@ __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x,
     uint32_t v[32];
     if constexpr (DT == kBF16) {
       uint32_t d[16];
-      load_bf16_block(x, b, d);
+      load_block16(x, b, d);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         v[2 * k] = d[k] << 16;

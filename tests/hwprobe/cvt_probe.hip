@@ -8,6 +8,8 @@
 
 typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x32 __attribute__((ext_vector_type(32)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -26,6 +28,18 @@ __global__ void k_q_fp6_bf16(int kind, const uint32_t* in, const uint8_t* sb, ui
   bf16x32 v = __builtin_bit_cast(bf16x32, u);
   u32x6 r = kind == 0 ? __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(v, scale_of(sb[i]))
                       : __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(v, scale_of(sb[i]));
+  for (int k = 0; k < 6; ++k) out[6 * i + k] = r[k];
+}
+
+// 32 fp16 (16 dwords) -> 32 fp6 codes (6 dwords); kind 0: E2M3, 1: E3M2
+__global__ void k_q_fp6_f16(int kind, const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  u32x16 u;
+  for (int k = 0; k < 16; ++k) u[k] = in[16 * i + k];
+  f16x32 v = __builtin_bit_cast(f16x32, u);
+  u32x6 r = kind == 0 ? __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(v, scale_of(sb[i]))
+                      : __builtin_amdgcn_cvt_scalef32_pk32_bf6_f16(v, scale_of(sb[i]));
   for (int k = 0; k < 6; ++k) out[6 * i + k] = r[k];
 }
 
@@ -52,6 +66,16 @@ __global__ void k_q_fp8_bf16(const uint32_t* in, const uint8_t* sb, uint32_t* ou
   out[i] = __builtin_bit_cast(uint32_t, r);
 }
 
+// 2 fp16 (one dword) -> 2 E4M3 codes (low 16 bits of the result)
+__global__ void k_q_fp8_f16(const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  f16x2 v = __builtin_bit_cast(f16x2, in[i]);
+  shortx2 old = {0, 0};
+  shortx2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(old, v, scale_of(sb[i]), false);
+  out[i] = __builtin_bit_cast(uint32_t, r);
+}
+
 // 2 fp32 -> 2 E4M3 codes
 __global__ void k_q_fp8_f32(const float* in, const uint8_t* sb, uint32_t* out, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -67,6 +91,14 @@ __global__ void k_q_fp4_bf16(const uint32_t* in, const uint8_t* sb, uint32_t* ou
   if (i >= n) return;
   bf16x2 v = __builtin_bit_cast(bf16x2, in[i]);
   out[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, v, scale_of(sb[i]), 0);
+}
+
+// 2 fp16 -> 2 E2M1 codes (low byte)
+__global__ void k_q_fp4_f16(const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  f16x2 v = __builtin_bit_cast(f16x2, in[i]);
+  out[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(0u, v, scale_of(sb[i]), 0);
 }
 
 // 2 fp32 -> 2 E2M1 codes (low byte)
@@ -136,6 +168,12 @@ int probe_q_fp6_bf16(int kind, const uint32_t* in, const uint8_t* sb, uint32_t* 
   hipLaunchKernelGGL(k_q_fp6_bf16, GRID(n), kind, in, sb, out, n); return (int)hipDeviceSynchronize(); }
 int probe_q_fp6_f32(int kind, const float* in, const uint8_t* sb, uint32_t* out, int n) {
   hipLaunchKernelGGL(k_q_fp6_f32, GRID(n), kind, in, sb, out, n); return (int)hipDeviceSynchronize(); }
+int probe_q_fp6_f16(int kind, const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  hipLaunchKernelGGL(k_q_fp6_f16, GRID(n), kind, in, sb, out, n); return (int)hipDeviceSynchronize(); }
+int probe_q_fp8_f16(const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  hipLaunchKernelGGL(k_q_fp8_f16, GRID(n), in, sb, out, n); return (int)hipDeviceSynchronize(); }
+int probe_q_fp4_f16(const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
+  hipLaunchKernelGGL(k_q_fp4_f16, GRID(n), in, sb, out, n); return (int)hipDeviceSynchronize(); }
 int probe_q_fp8_bf16(const uint32_t* in, const uint8_t* sb, uint32_t* out, int n) {
   hipLaunchKernelGGL(k_q_fp8_bf16, GRID(n), in, sb, out, n); return (int)hipDeviceSynchronize(); }
 int probe_q_fp8_f32(const float* in, const uint8_t* sb, uint32_t* out, int n) {

@@ -2,13 +2,15 @@
 relies on, against the brute-force nearest-code search (tests/brute.py).
 
 Each instruction runs in a test-only kernel (tests/hwprobe/cvt_probe.hip) on
-every finite bf16 pattern under every finite scale byte (0..254), or on every
-code under every scale byte for the reverse direction.  The library uses an
+every finite bf16 or fp16 pattern under every finite scale byte (0..254), on
+every fp32 rounding class under every byte, or on every code under every
+scale byte for the reverse direction.  The library uses an
 instruction only for the cases asserted here:
 
-  quantize   from bf16 (E2M3 / E3M2 32-wide, E2M1 and E4M3 pairwise): every
-             finite bf16 pattern under every byte 0..254, bit-exact,
-             saturation included.
+  quantize   from bf16 and from fp16 (E2M3 / E3M2 32-wide, E2M1 and E4M3
+             pairwise): every finite bf16 or fp16 pattern under every byte
+             0..254, bit-exact, saturation included (E4M3 within the
+             block domain, as below).
              from fp32 (E2M3 / E3M2 as two 16-wide operands whose values
              land at the even and odd code positions; E2M1 and E4M3
              pairwise): every rounding class under every byte 0..254.  A
@@ -21,7 +23,7 @@ instruction only for the cases asserted here:
              the lowest, the highest or all of them set, and both signs:
              522,240 values x 255 bytes per form, bit-exact for every value
              a block can hold (|v| / X < 2^(emax + 1)).
-             E4M3 (bf16 and fp32): bit-exact for |v| / X < 512 once a
+             E4M3 (bf16, fp16 and fp32): bit-exact for |v| / X < 512 once a
              rounded magnitude of 0x7F (the instruction does not saturate)
              is replaced by 0x7E (448).
   dequantize every code under scale bytes 0..254 is the exact product
@@ -56,9 +58,11 @@ def lib():
         hb.build()
     lib = ctypes.CDLL(path)
     P, I = ctypes.c_void_p, ctypes.c_int
-    for f in ("probe_q_fp6_bf16", "probe_q_fp6_f32", "probe_dq_fp6_bf16", "probe_dq_fp6_f32"):
+    for f in ("probe_q_fp6_bf16", "probe_q_fp6_f32", "probe_q_fp6_f16", "probe_dq_fp6_bf16",
+              "probe_dq_fp6_f32"):
         getattr(lib, f).argtypes = [I, P, P, P, I]
     for f in ("probe_q_fp8_bf16", "probe_q_fp8_f32", "probe_q_fp4_bf16", "probe_q_fp4_f32",
+              "probe_q_fp8_f16", "probe_q_fp4_f16",
               "probe_dq_fp8_bf16", "probe_dq_fp4_bf16", "probe_dq_fp8_f32", "probe_dq_fp4_f32"):
         getattr(lib, f).argtypes = [P, P, P, I]
     return lib
@@ -73,6 +77,11 @@ def all_bf16():
     with np.errstate(invalid="ignore"):
         v = workloads.bf16_bits_to_f32(b).astype(np.float64)
     return b, v
+
+
+def all_f16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return b, b.view(np.float16).astype(np.float64)
 
 
 def fp32_set():
@@ -170,16 +179,18 @@ def in_range(vals, byte_of, fmt):
 # ----------------------------------------------------------------------------
 # quantize direction
 # ----------------------------------------------------------------------------
+@pytest.mark.parametrize("src", ["bf16", "f16"])
 @pytest.mark.parametrize("kind,fmt", [(0, E2M3), (1, E3M2)], ids=["e2m3", "e3m2"])
-def test_pk32_fp6_from_bf16_all_patterns_all_scales(lib, kind, fmt):
-    b, v = all_bf16()
+def test_pk32_fp6_from_16bit_all_patterns_all_scales(lib, kind, fmt, src):
+    b, v = all_bf16() if src == "bf16" else all_f16()
     fin = np.isfinite(v)
     lanes = 65536 // 32
     inp = np.tile(b.reshape(lanes, 32).view(np.uint32).reshape(lanes, 16), (255, 1))
     sb = np.repeat(BYTES, lanes)
     d_in, d_sb = dev(inp), dev(sb)
     out = torch.zeros(inp.shape[0] * 6, dtype=torch.int32, device="cuda")
-    assert lib.probe_q_fp6_bf16(kind, d_in.data_ptr(), d_sb.data_ptr(), out.data_ptr(), inp.shape[0]) == 0
+    fn = lib.probe_q_fp6_bf16 if src == "bf16" else lib.probe_q_fp6_f16
+    assert fn(kind, d_in.data_ptr(), d_sb.data_ptr(), out.data_ptr(), inp.shape[0]) == 0
     got = unpack_stream(out.cpu().numpy().view(np.uint32).reshape(-1, 6), 6, 32).reshape(-1)
     vals = np.tile(v, 255)
     byte_of = np.repeat(BYTES, 65536)
@@ -236,18 +247,19 @@ def test_2xpk16_fp6_from_fp32(lib, kind, fmt):
     assert bad.size == 0, (bad.size, vals[bad[:5]], byte_of[bad[:5]], got[bad[:5]], want[bad[:5]])
 
 
-@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("src", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("fmt", [E2M1, E4M3], ids=["e2m1", "e4m3"])
 def test_pk_fp4_fp8_pairs(lib, src, fmt):
-    if src == "bf16":
-        b, v = all_bf16()
+    if src in ("bf16", "f16"):
+        b, v = all_bf16() if src == "bf16" else all_f16()
         fin = np.isfinite(v)
         words = b.reshape(-1, 2).view(np.uint32).reshape(-1)
         inp = np.tile(words, 255)
         sb = np.repeat(BYTES, words.size)
         vals = np.tile(v, 255)
         byte_of = np.repeat(BYTES, 65536)
-        fn = lib.probe_q_fp4_bf16 if fmt == E2M1 else lib.probe_q_fp8_bf16
+        fn = {("bf16", E2M1): lib.probe_q_fp4_bf16, ("bf16", E4M3): lib.probe_q_fp8_bf16,
+              ("f16", E2M1): lib.probe_q_fp4_f16, ("f16", E4M3): lib.probe_q_fp8_f16}[src, fmt]
         n = inp.size
     else:
         s = fp32_set()

@@ -12,6 +12,7 @@ checkpoints, activations and attention scores, which are not available):
   axs6_weight    bf16 [4096, 4096], N(0, 0.02^2), 0.1% of the
                  entries multiplied by 50 (outliers)             (seed 2)
   linear_weight  bf16 [14336, 4096], N(0, 0.02^2)                (seed 3)
+                 (linear_weight_f16: the same draw rounded to fp16)
   attn_scores    fp32 [32*4096, 4096] (32 heads x 4096 queries
                  x 4096 keys), N(0, 3^2)                         (seed 4)
   activations    bf16 [16384, 8192], 0.5 * Student-t(nu=3); 1% of
@@ -70,6 +71,13 @@ def linear_weight(rows=14336, cols=4096, seed=None) -> np.ndarray:
     rng = np.random.default_rng(SEEDS["linear_weight"] if seed is None else seed)
     x = (0.02 * rng.standard_normal((rows, cols))).astype(np.float32)
     return to_bf16_bits(x)
+
+
+def linear_weight_f16(rows=14336, cols=4096, seed=None) -> np.ndarray:
+    """linear_weight's draw rounded to fp16 (numpy's nearest-even cast)
+    instead of bf16: the same weight as an FP16 checkpoint would hold it."""
+    rng = np.random.default_rng(SEEDS["linear_weight"] if seed is None else seed)
+    return (0.02 * rng.standard_normal((rows, cols))).astype(np.float32).astype(np.float16)
 
 
 def attn_scores(rows=32 * 4096, cols=4096, seed=None) -> np.ndarray:
