@@ -1,8 +1,8 @@
 """Property-based pins of the oracle's quantizer (CPU only).
 
-hypothesis draws whole 32-value blocks -- arbitrary bf16 bit patterns (NaN,
-inf, subnormals, signed zeros included) or fp32 values spread over many
-binades -- and every block must quantize exactly as the brute-force checker
+hypothesis draws whole 32-value blocks -- arbitrary bf16 or fp16 bit
+patterns (NaN, inf, subnormals, signed zeros included) or fp32 values spread
+over many binades -- and every block must quantize exactly as the brute-force checker
 in brute.py says: the scale byte by comparison with powers of two, every
 code by exhaustive nearest-grid-point search, the packing bit by bit.  The
 checker shares no arithmetic with the oracle.
@@ -67,4 +67,23 @@ def test_dequantize_of_quantize_is_fake_quantize(fmt, bits):
     x = np.asarray(bits, np.uint16).reshape(1, 32)
     codes, scales, aux = oracle.quantize(fmt, x)
     y = oracle.dequantize(fmt, codes, scales, aux, 1, 32, oracle.BF16)
+    assert np.array_equal(y.view(np.uint16), oracle.fake_quantize(fmt, x).view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", MX + EXMY[3::4], ids=lambda f: hex(f))
+@SETTINGS
+@given(bits=bf16_block)
+def test_fp16_blocks_vs_brute_force(fmt, bits):
+    # the same 16-bit patterns read as binary16 (numpy widens them exactly)
+    x = np.asarray(bits, np.uint16).view(np.float16)
+    _check_block(fmt, x, x.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", MX + EXMY[3::4], ids=lambda f: hex(f))
+@SETTINGS
+@given(bits=bf16_block)
+def test_fp16_dequantize_of_quantize_is_fake_quantize(fmt, bits):
+    x = np.asarray(bits, np.uint16).view(np.float16).reshape(1, 32)
+    codes, scales, aux = oracle.quantize(fmt, x)
+    y = oracle.dequantize(fmt, codes, scales, aux, 1, 32, oracle.F16)
     assert np.array_equal(y.view(np.uint16), oracle.fake_quantize(fmt, x).view(np.uint16))
