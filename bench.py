@@ -601,6 +601,11 @@ def secondary(mx, steps, threads, check=True):
     # -- the same scores inside a fused attention forward: 32 heads x 4096
     #    queries x 4096 keys, d = 128, bf16 q/k, V^T in MXFP8, bf16 output
     S.res.update(attention_line(mx, S.k))
+    if check:
+        for name, ok in attention_parity(mx).items():
+            S.res[name]["parity"] = ok
+            if not ok["bit_exact"]:
+                S.failed.append(name)
 
     # -- layer-by-layer conversion of a synthetic dense decoder (4 layers,
     #    hidden 4096, MLP 14336, 1024-wide k/v): weights already on the
@@ -719,6 +724,55 @@ def attention_line(mx, k, heads=32, lq=4096, lk=4096, d=128):
             "valu_frac": round(ops_per * scores / ms / 1e9 / VALU_PEAK_TOPS, 4),
             "workload": f"{heads} heads x {lq} queries x {lk} keys, d {d}, bf16 q/k, MXFP8 V^T, "
                         "bf16 out"}
+    return out
+
+
+# sampled (head, query) rows of the attention parity check
+ATTN_ROWS = [(0, 0), (5, 1234), (17, 4095), (31, 2048), (12, 77), (31, 4095), (8, 3000),
+             (20, 511)]
+
+
+def attention_parity(mx, heads=32, lq=4096, lk=4096, d=128):
+    """Both attention forwards in the benchmark's launch configuration (32
+    heads x 4096 x 4096, d 128, MXFP8 V^T, bf16 output) on exactly summable
+    scores: q and k entries are multiples of 1/4 in [-3, 3], so every score
+    is exact in fp32 whatever the order of the sums, and the sampled rows'
+    probability blocks, scale bytes and row maxima must equal the oracle's
+    bit for bit.  (The output o rounds differently by construction -- fp32
+    matrix-core sums against the oracle's double -- and is checked against
+    its derived bound in the GPU tests.)"""
+    import numpy as np
+    import torch
+
+    import oracle
+    g = torch.Generator(device="cuda").manual_seed(13)
+    qd = (torch.randint(-12, 13, (heads, lq, d), generator=g, device="cuda").float() / 4).to(
+        torch.bfloat16)
+    kd = (torch.randint(-12, 13, (heads, lk, d), generator=g, device="cuda").float() / 4).to(
+        torch.bfloat16)
+    vc, vs = mx.quantize_v(torch.randn(heads, lk, d, generator=g, device="cuda"), "mxfp8")
+    q, k = host(qd), host(kd)
+    vch, vsh = host(vc).reshape(heads, -1), host(vs).reshape(heads, -1)
+    scale = np.float32(d ** -0.5)
+    out = {}
+    for name, efq in (("attention_fwd_e2m1_p_mxfp8_v", False),
+                      ("attention_fwd_efq_e2m1_p_mxfp8_v", True)):
+        _, rm, _, pc, ps = mx.attention_fwd(qd, kd, vc, vs, "mxfp8", scale=scale,
+                                            out_dtype=torch.bfloat16, stats=True, probs=True,
+                                            efq=efq)
+        torch.cuda.synchronize()
+        ok = True
+        for h, i in ATTN_ROWS:
+            _, rm_ref, _, pc_ref, ps_ref = oracle.attention_fwd(
+                oracle.FP8_E4M3, q[h:h + 1, i:i + 1], k[h:h + 1], vch[h:h + 1], vsh[h:h + 1],
+                scale, 64, oracle.FP32, efq=efq)
+            ok &= bool(np.array_equal(host(pc[h, i]), pc_ref[0, 0])
+                       and np.array_equal(host(ps[h, i]), ps_ref[0, 0])
+                       and float(rm[h, i]) == float(rm_ref[0, 0]))
+        out[name] = {"bit_exact": ok,
+                     "compared": f"{len(ATTN_ROWS)} sampled rows on exactly summable q and k: "
+                                 "probability blocks, scale bytes, row maxima"}
+        del rm, pc, ps
     return out
 
 
