@@ -1,17 +1,18 @@
 // mx_kernels.hip -- gfx950 kernels for block-shared-exponent quantization.
 //
 // Layout: one lane owns one 32-value block.  The lane reads its block (64 B
-// of bf16 or 128 B of fp32) with 128-bit loads, reduces the largest
+// of bf16 or fp16, 128 B of fp32) with 128-bit loads, reduces the largest
 // magnitude in registers, derives the shared scale byte, converts the 32
 // values with the scaled-convert instructions (FP6: one 32-wide instruction;
 // FP4/FP8: one per pair) or, for AXS-6, with integer/fp32 arithmetic, and
 // writes its packed codes (24/16/32 B) and its scale byte.  No arithmetic
-// crosses lanes, so every output byte has exactly one writer.  Wide outputs
-// (and the bf16 fake-quantize inputs) pass through a per-wave LDS tile of 64
-// blocks for coalesced 1 KB accesses; a wave has read its whole tile before
-// it writes any of it, so in-place fake-quantization is safe.  The
-// exp-then-quantize kernel is the exception: there two lanes share a block
-// (see its section below).
+// crosses lanes, so every output byte has exactly one writer.  Wide outputs,
+// and the 16-bit inputs of the MX quantizers and of the MX and AXS-6
+// fake-quantizers, pass through a per-wave LDS tile of 64 blocks for
+// coalesced 1 KB accesses; a wave has read its whole tile before it writes
+// any of it, so in-place fake-quantization is safe.  The exp-then-quantize
+// kernel is the exception: there two lanes share a block (see its section
+// below).
 //
 // Rules: "Online MXFP6" page ("Start a model": packed codes and an E8M0
 // scale per 32 values); "EFQ-Softmax" explainer (exponent-only block scale
@@ -191,9 +192,11 @@ __device__ __forceinline__ void store_tile_via_lds(uint4* __restrict__ lds, void
 // ---------------------------------------------------------------------------
 // Tensor element types, as the C ABI's mx_dtype.  fp16 tensors (the "Online
 // MXFP6" page, "Start a model": BF16 or FP16 weights) have bf16's 64-byte
-// blocks; their values are widened to fp32 in registers (exactly) and take
-// the fp32 paths, and fp32 results leave rounded once to binary16 (nearest
-// even, overflow to infinity; the canonical fp32 NaN becomes 0x7E00).
+// blocks.  The MX encoders take fp16 values directly (the fp16-source
+// scaled conversions); AXS-6 and eXmY widen them to fp32 in registers
+// (exactly) and take the fp32 paths.  fp16 outputs are fp32 results rounded
+// once to binary16 (nearest even, overflow to infinity; the canonical fp32
+// NaN becomes 0x7E00).
 // ---------------------------------------------------------------------------
 constexpr int kBF16 = 0, kF32 = 1, kF16 = 2;
 
