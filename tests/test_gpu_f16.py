@@ -173,3 +173,21 @@ def test_f16_outputs_stay_in_bounds(mx, fmt, nblocks):
                             torch.from_numpy(oa).cuda() if fmt == oracle.AXS6 else None,
                             nblocks, 32, mx.MX_FP16, ybuf[guard:guard + n]) == 0
     check(oracle.dequantize(fmt, oc, os_, oa, nblocks, 32, oracle.F16), "dq")
+
+
+@pytest.mark.parametrize("fmt", oracle.EXMY_FORMATS, ids=lambda f: f"e{(f >> 4) & 15}m{f & 15}")
+def test_every_exmy_split_on_every_f16_pattern(mx, fmt):
+    # quantize and fake-quantize of every finite fp16 pattern under three
+    # anchors, for each of the 42 splits of 3 to 9 bits
+    allv = all_finite_f16()
+    absv = np.abs(allv.astype(np.float64))
+    x = np.concatenate([anchored_blocks(allv[absv < 2.0 ** (E + 1)], E) for E in (-14, 0, 15)])
+    xd = dev16(x)
+    codes, scales, _ = mx.quantize(xd, fmt)
+    fq = mx.fake_quantize(xd, fmt)
+    torch.cuda.synchronize()
+    oc, os_, _ = oracle.quantize(fmt, x)
+    assert_bytes_equal(to_host(scales), os_, "scales")
+    assert_bytes_equal(to_host(codes), oc, "codes", oracle.BYTES_PER_BLOCK[fmt])
+    want = oracle.fake_quantize(fmt, x)
+    assert_bytes_equal(to_host(fq).view(np.uint16), want.view(np.uint16), "fake-quantized", 64)
