@@ -8,7 +8,6 @@ quantize and the exp-then-quantize rows (with the fp32 dequantization of
 the probabilities): sampled rows before and after the 2^31-byte mark are
 compared with the oracle bit for bit.
 """
-import numpy as np
 import pytest
 import torch
 
