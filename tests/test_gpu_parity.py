@@ -9,7 +9,6 @@ import numpy as np
 import pytest
 import torch
 
-import brute
 import oracle
 import workloads
 from gpu_util import assert_bytes_equal, to_dev, to_host

@@ -6,7 +6,6 @@ dropped term, a wrong sign, a wrong index or a transposed operand anywhere in
 oracle/mxref.c fails at least one of them.
 """
 import json
-import math
 import os
 import re
 
