@@ -1,9 +1,10 @@
 """Bit-exact parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Small and ragged shapes are compared element by element; the full-size
-workloads are compared on sampled rows plus properties that hold at any
-size.  Every comparison is bytewise: codes, scales, the AXS-6 config plane,
-and dequantized / fake-quantized values (exact power-of-two products).
+Small and ragged shapes, every finite bf16 pattern and arbitrary code and
+scale bytes are compared element by element (the full-size workloads, whole
+tensors, are in test_gpu_full.py).  Every comparison is bytewise: codes,
+scales, the AXS-6 config plane, and dequantized / fake-quantized values
+(exact power-of-two products).
 """
 import numpy as np
 import pytest
