@@ -229,7 +229,8 @@ mx_status mx_softmax_quantize(mx_format fmt, int block, const float *s,
  *             most 2^24; heads == 0 or lq == 0 is a no-op
  *   scale     score multiplier (typically 1/sqrt(d)): positive, with
  *             scale * log2 e finite (MX_ERR_VALUE otherwise)
- *   o         [heads, lq, d] of out_dtype
+ *   o         [heads, lq, d] of out_dtype (MX_BF16 or MX_FP32; MX_FP16
+ *             gives MX_ERR_UNSUPPORTED)
  *   row_max, row_sum    [heads, lq] fp32: the row's largest fp32(s * scale)
  *             (NaN scores skipped) and the final denominator (the sum of
  *             the E2M1 probabilities relative to 2^(max t)); may be NULL
