@@ -670,16 +670,20 @@ __global__ __launch_bounds__(256) void dequantize_axs6(const void* __restrict__ 
 // ---------------------------------------------------------------------------
 template <bool M0>
 __device__ __forceinline__ uint32_t exmy_round(float a, const ExmyParams& p) {
-  // a >= 0, at most the largest magnitude.  The grid step at a is 2^(et -
-  // 127 - m) with et = max(a's biased exponent, 127 + emin); adding C =
-  // 2^(et - 127 + 23 - m) leaves a rounded to that step (nearest, ties to
-  // even) in the low mantissa bits of the sum, and the binade's first code
-  // is (et - 127 - emin) << m.
+  // a >= 0, at most the largest magnitude.  eb = max(a's biased exponent,
+  // 127 + emin) - (127 + emin), one saturating subtraction: which of the
+  // format's binades holds a (0 also below 2^emin, where the codes are
+  // subnormal).  The grid step at a is 2^(eb + emin - m); adding C =
+  // 2^(eb + emin + 23 - m) leaves a rounded to that step (nearest, ties to
+  // even) as the sum's mantissa field (the sum lies in [C, 2C)), and the
+  // binade's first code is eb << m.  C's exponent field is eb plus a
+  // constant of the format, kept in a scalar register.
   const uint32_t ab = __float_as_uint(a);
   const uint32_t emin_b = (uint32_t)(127 + p.emin);
-  const uint32_t et = max(ab >> 23, emin_b);
-  const float C = __uint_as_float((et + (uint32_t)(23 - p.m)) << 23);
-  uint32_t mag = __float_as_uint(a + C) - __float_as_uint(C) + ((et - emin_b) << p.m);
+  const uint32_t eb = __builtin_elementwise_sub_sat(ab >> 23, emin_b);
+  const uint32_t c0 = __builtin_amdgcn_readfirstlane((emin_b + (uint32_t)(23 - p.m)) << 23);
+  const float C = __uint_as_float((eb << 23) + c0);
+  uint32_t mag = (__float_as_uint(a + C) & 0x7FFFFFu) + (eb << p.m);
   if constexpr (M0) {
     // exponent-only formats: a tie between two powers of two goes to the
     // even exponent field, which the adder does not know about
@@ -777,21 +781,30 @@ __global__ __launch_bounds__(256) void quantize_exmy(const void* __restrict__ x,
     for (int j = 0; j < W; ++j) codes[b * W + j] = byte == 0xFFu ? 0u : o[j];  // 4W bytes
     scales[b] = (uint8_t)byte;
   };
-  // one block per lane with direct loads: with this kernel's software
-  // rounding the wave-tile loads of quantize_mx measured 1.6 % slower
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-    uint32_t v[32];
-    if constexpr (DT == kBF16) {
-      uint32_t d[16];
-      load_block16(x, b, d);
+  if constexpr (DT != kF32) {
+    // bf16 and fp16 input: one wave tile of 64 blocks per wave (wave_tile16)
+    __shared__ uint4 lds[4][4 * kTile];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t * kTile < nb; t += nwaves)
+      wave_tile16(x, t, nb, lds[wave], lane, [&](int64_t b, const uint32_t (&d)[16]) {
+        uint32_t v[32];
+        if constexpr (DT == kBF16) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        v[2 * k] = d[k] << 16;
-        v[2 * k + 1] = d[k] & 0xFFFF0000u;
-      }
-      block(b, v, exmy_byte_from_amax(amax_bf16x32(d), p));
-    } else {
+          for (int k = 0; k < 16; ++k) {
+            v[2 * k] = d[k] << 16;
+            v[2 * k + 1] = d[k] & 0xFFFF0000u;
+          }
+          block(b, v, exmy_byte_from_amax(amax_bf16x32(d), p));
+        } else {
+          widen_f16(d, v);
+          block(b, v, exmy_byte_from_amax(amax_f16x32(d), p));
+        }
+      });
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+      uint32_t v[32];
       load_wide<DT>(x, b, v);
       block(b, v, exmy_byte_from_amax(amax_f32x32(v), p));
     }
